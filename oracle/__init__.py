@@ -1,0 +1,186 @@
+"""CPU oracle for the mask-only logits path -- TEST INFRASTRUCTURE ONLY.
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg import this
+package.  The product path (the HIP library and its Python binding) never does,
+and nothing here is shared with it.  The arithmetic lives in ``oracle.c`` (plain C,
+fp64, OpenMP over output elements); this module compiles it with gcc and marshals
+numpy arrays into it.
+
+Every function here is pinned by CPU tests to something other than itself
+(library routines, brute force, closed forms and exact-integer results); the
+pins are listed in the test modules ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_DIR = Path(__file__).resolve().parent
+_SRC = _DIR / "oracle.c"
+_LIB = _DIR / "liboracle.so"
+_lib = None
+
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_p = ctypes.c_void_p
+
+
+def build(force: bool = True) -> Path:
+    """Compile oracle.c into oracle/liboracle.so with gcc and OpenMP."""
+    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+        tmp = _LIB.with_suffix(".so.tmp")
+        cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+               "-Wall", "-Wextra", "-o", str(tmp), str(_SRC)]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+            build(force=True)
+        lib = ctypes.CDLL(str(_LIB))
+        lib.oracle_mask_compact.restype = _i64
+        lib.oracle_mask_compact.argtypes = [_p, _i64, _i32, _p]
+        lib.oracle_mask_compact_flags.restype = _i64
+        lib.oracle_mask_compact_flags.argtypes = [_p, _i64, _p]
+        lib.oracle_mask_compact_batched.restype = _i64
+        lib.oracle_mask_compact_batched.argtypes = [_p, _p, _i32, _i32, _p, _p]
+        lib.oracle_num_chunks.restype = _i64
+        lib.oracle_num_chunks.argtypes = [_i64, _i64]
+        lib.oracle_chunk_range.restype = None
+        lib.oracle_chunk_range.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+        for name in ("oracle_masked_logits_bf16", "oracle_masked_logits_f32"):
+            f = getattr(lib, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [_p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+        lib.oracle_masked_logits_chunked_bf16.restype = ctypes.c_int
+        lib.oracle_masked_logits_chunked_bf16.argtypes = [_p, _i64, _i64, _p, _i64, _p, _i64, _i64, _p]
+        lib.oracle_logits_bytes.restype = _i64
+        lib.oracle_logits_bytes.argtypes = [_i64, _i64, _i64]
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def _np(x, dtype=None):
+    """numpy view of a CPU torch tensor or array (bf16 as its uint16 bit pattern)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().contiguous()
+            if x.dtype == torch.bfloat16:
+                x = x.view(torch.int16).numpy().view(np.uint16)
+            else:
+                x = x.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    x = np.ascontiguousarray(x)
+    if dtype is not None:
+        x = np.ascontiguousarray(x, dtype=dtype)
+    return x
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def logits_bytes(rows: int, V: int, esize: int) -> int:
+    """rows * V * esize, or -1 on int64 overflow."""
+    return int(_load().oracle_logits_bytes(int(rows), int(V), int(esize)))
+
+
+def mask_compact(tokens, mask_id: int) -> np.ndarray:
+    """Ascending positions p with tokens[p] == mask_id (int32)."""
+    t = _np(tokens, np.int32)
+    idx = np.empty(max(1, t.size), np.int32)
+    m = _load().oracle_mask_compact(_ptr(t), t.size, int(mask_id), _ptr(idx))
+    return idx[:m].copy()
+
+
+def mask_compact_flags(flags) -> np.ndarray:
+    f = _np(flags, np.uint8)
+    idx = np.empty(max(1, f.size), np.int32)
+    m = _load().oracle_mask_compact_flags(_ptr(f), f.size, _ptr(idx))
+    return idx[:m].copy()
+
+
+def mask_compact_batched(tokens, seq_offsets, mask_id: int):
+    """(idx, idx_offsets) for a ragged batch; idx holds global positions."""
+    t = _np(tokens, np.int32)
+    so = _np(seq_offsets, np.int32)
+    nseq = so.size - 1
+    idx = np.empty(max(1, t.size), np.int32)
+    off = np.empty(nseq + 1, np.int32)
+    m = _load().oracle_mask_compact_batched(_ptr(t), _ptr(so), nseq, int(mask_id), _ptr(idx), _ptr(off))
+    return idx[:m].copy(), off
+
+
+def num_chunks(M: int, C: int) -> int:
+    return int(_load().oracle_num_chunks(int(M), int(C)))
+
+
+def chunk_range(M: int, C: int, k: int):
+    r0, r1 = _i64(), _i64()
+    _load().oracle_chunk_range(int(M), int(C), int(k), ctypes.byref(r0), ctypes.byref(r1))
+    return int(r0.value), int(r1.value)
+
+
+def masked_logits(H, idx, W, rows=None) -> np.ndarray:
+    """fp64 logits [len(rows), V] of output rows `rows` (default: all M rows).
+
+    H [L, d] and W [V, d] are bf16 or fp32 (CPU torch tensors or numpy arrays;
+    numpy uint16 means bf16 bit patterns)."""
+    import torch
+    is_bf16 = (isinstance(H, torch.Tensor) and H.dtype == torch.bfloat16) or \
+              (isinstance(H, np.ndarray) and H.dtype == np.uint16)
+    if is_bf16:
+        h = _np(H, np.uint16)
+        w = _np(W, np.uint16)
+        f = _load().oracle_masked_logits_bf16
+    else:
+        h = _np(H, np.float32)
+        w = _np(W, np.float32)
+        f = _load().oracle_masked_logits_f32
+    L, d = h.shape
+    V = w.shape[0]
+    assert w.shape[1] == d
+    ix = _np(idx, np.int32)
+    M = ix.size
+    r = np.arange(M, dtype=np.int64) if rows is None else _np(rows, np.int64)
+    out = np.empty((r.size, V), np.float64)
+    if r.size == 0 or V == 0:
+        return out
+    rc = f(_ptr(h), L, d, _ptr(ix), M, _ptr(w), V, _ptr(r), r.size, _ptr(out))
+    if rc != 0:
+        raise IndexError("row or index out of range")
+    return out
+
+
+def masked_logits_chunked(H, idx, W, chunk_rows: int) -> np.ndarray:
+    """The micro-batched LM head (bf16 only): slices of chunk_rows rows, concatenated."""
+    h = _np(H, np.uint16)
+    w = _np(W, np.uint16)
+    L, d = h.shape
+    V = w.shape[0]
+    ix = _np(idx, np.int32)
+    M = ix.size
+    out = np.empty((M, V), np.float64)
+    if M == 0:
+        return out
+    rc = _load().oracle_masked_logits_chunked_bf16(_ptr(h), L, d, _ptr(ix), M, _ptr(w), V,
+                                                   int(chunk_rows), _ptr(out))
+    if rc != 0:
+        raise IndexError("index out of range")
+    return out

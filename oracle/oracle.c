@@ -1,0 +1,213 @@
+/*
+ * CPU oracle for the mask-only logits path -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+ * load this library.  The product path (the HIP library and its binding) never
+ * links, loads or calls it.  It shares no code, header or table with the HIP path.
+ *
+ * What it computes is the plain definition of each step, written out:
+ *
+ *  (1) compaction -- the list of masked positions in ascending order.  The pages
+ *      take "the mask indices" as an input of the fused kernel ("Mosaic: Unlocking
+ *      Long-Context Inference for Diffusion LLMs via Global Memory" review, 核心组件
+ *      1. Mask-only Logits Kernel; "扩散大语言模型内存优化：Mosaic系统突破与实践",
+ *      §2.2 indirect addressing through the mask index).  Ascending order is the
+ *      reading taken where the pages are silent.
+ *
+ *  (2) chunk partition -- dLLM-Serve's logit budget ("扩散大语言模型内存优化：从理论
+ *      到系统设计", §3.2.2): when the number of rows that need logits exceeds
+ *      max_num_logits, rows are processed in consecutive micro-batches of at most
+ *      max_num_logits rows and the results are concatenated in order.
+ *
+ *  (3) logits -- the LM head applied to the masked rows only: row i of the output is
+ *      H[idx[i], :] . W^T (Mosaic review, 核心观察 #2: only masked tokens are sampled,
+ *      so logits are computed for them alone; the Mosaic abstract states that the
+ *      system preserves exact model outputs, so these rows equal the dense logits'
+ *      rows).  Each element is an fp64 sum over k in ascending order of exact fp64
+ *      products (bf16 and fp32 inputs convert to fp64 exactly; products of two bf16
+ *      or two fp32 values are exact in fp64).  No bias, scale or softcap: the pages
+ *      name only the lm_head projection.
+ *
+ * Parallelism: OpenMP over output elements.  It does not change any arithmetic;
+ * every element is still one ascending-k fp64 sum.
+ */
+#include <stdint.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- (1) compaction */
+
+/* idx[0..M) = ascending p in [0, L) with tokens[p] == mask_id.  Returns M. */
+int64_t oracle_mask_compact(const int32_t *tokens, int64_t L, int32_t mask_id, int32_t *idx)
+{
+    int64_t m = 0;
+    for (int64_t p = 0; p < L; ++p)
+        if (tokens[p] == mask_id)
+            idx[m++] = (int32_t)p;
+    return m;
+}
+
+/* Same, with a flag array: position p is masked when flags[p] != 0. */
+int64_t oracle_mask_compact_flags(const uint8_t *flags, int64_t L, int32_t *idx)
+{
+    int64_t m = 0;
+    for (int64_t p = 0; p < L; ++p)
+        if (flags[p] != 0)
+            idx[m++] = (int32_t)p;
+    return m;
+}
+
+/* Ragged batch over concatenated sequences: sequence s owns positions
+ * [seq_offsets[s], seq_offsets[s+1]).  idx holds global positions, sequence by
+ * sequence; idx_offsets[s] is where sequence s starts in idx, idx_offsets[nseq] = M. */
+int64_t oracle_mask_compact_batched(const int32_t *tokens, const int32_t *seq_offsets, int32_t nseq,
+                                    int32_t mask_id, int32_t *idx, int32_t *idx_offsets)
+{
+    int64_t m = 0;
+    for (int32_t s = 0; s < nseq; ++s) {
+        idx_offsets[s] = (int32_t)m;
+        for (int64_t p = seq_offsets[s]; p < seq_offsets[s + 1]; ++p)
+            if (tokens[p] == mask_id)
+                idx[m++] = (int32_t)p;
+    }
+    idx_offsets[nseq] = (int32_t)m;
+    return m;
+}
+
+/* ---------------------------------------------------------- (2) chunk partition */
+
+/* Number of micro-batches for M rows with at most C rows each.  C <= 0 means no
+ * limit.  M <= C is a single call of the LM head; M == 0 is no work. */
+int64_t oracle_num_chunks(int64_t M, int64_t C)
+{
+    if (M <= 0)
+        return 0;
+    if (C <= 0 || M <= C)
+        return 1;
+    return (M + C - 1) / C;
+}
+
+/* Rows [*r0, *r1) of chunk k: consecutive slices of C rows, the last one shorter. */
+void oracle_chunk_range(int64_t M, int64_t C, int64_t k, int64_t *r0, int64_t *r1)
+{
+    if (C <= 0 || M <= C) {
+        *r0 = 0;
+        *r1 = M;
+        return;
+    }
+    *r0 = k * C;
+    *r1 = (k + 1) * C < M ? (k + 1) * C : M;
+}
+
+/* ------------------------------------------------------------------ (3) logits */
+
+/* bfloat16 is the upper half of an IEEE-754 binary32: widen exactly. */
+static double bf16_value(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double lm_head_dot_bf16(const uint16_t *h_row, const uint16_t *w_row, int64_t d)
+{
+    double acc = 0.0;
+    for (int64_t k = 0; k < d; ++k)
+        acc += bf16_value(h_row[k]) * bf16_value(w_row[k]);
+    return acc;
+}
+
+static double lm_head_dot_f32(const float *h_row, const float *w_row, int64_t d)
+{
+    double acc = 0.0;
+    for (int64_t k = 0; k < d; ++k)
+        acc += (double)h_row[k] * (double)w_row[k];
+    return acc;
+}
+
+/* out[r][v] = logits of output row rows[r] (an index into idx[0..M)) against every
+ * vocabulary row v < V:  sum_k H[idx[rows[r]]][k] * W[v][k].  H is [L, d] and W is
+ * [V, d], both row-major bfloat16 bit patterns.  out is [nrows][V] fp64.
+ * Returns 0, or -1 when an index is out of range. */
+int oracle_masked_logits_bf16(const uint16_t *H, int64_t L, int64_t d, const int32_t *idx, int64_t M,
+                              const uint16_t *W, int64_t V, const int64_t *rows, int64_t nrows,
+                              double *out)
+{
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= M || idx[rows[r]] < 0 || idx[rows[r]] >= L)
+            return -1;
+    int64_t total = nrows * V;
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < total; ++e) {
+        int64_t r = e / V, v = e % V;
+        const uint16_t *h_row = H + (int64_t)idx[rows[r]] * d;
+        out[e] = lm_head_dot_bf16(h_row, W + v * d, d);
+    }
+    return 0;
+}
+
+int oracle_masked_logits_f32(const float *H, int64_t L, int64_t d, const int32_t *idx, int64_t M,
+                             const float *W, int64_t V, const int64_t *rows, int64_t nrows,
+                             double *out)
+{
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= M || idx[rows[r]] < 0 || idx[rows[r]] >= L)
+            return -1;
+    int64_t total = nrows * V;
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < total; ++e) {
+        int64_t r = e / V, v = e % V;
+        const float *h_row = H + (int64_t)idx[rows[r]] * d;
+        out[e] = lm_head_dot_f32(h_row, W + v * d, d);
+    }
+    return 0;
+}
+
+/* The chunked logits operator as dLLM-Serve's micro-batching describes it: run the
+ * LM head on each slice of at most C rows and concatenate the slices in order.
+ * out is [M][V] fp64. */
+int oracle_masked_logits_chunked_bf16(const uint16_t *H, int64_t L, int64_t d, const int32_t *idx,
+                                      int64_t M, const uint16_t *W, int64_t V, int64_t C, double *out)
+{
+    for (int64_t i = 0; i < M; ++i)
+        if (idx[i] < 0 || idx[i] >= L)
+            return -1;
+    int64_t K = oracle_num_chunks(M, C);
+    for (int64_t k = 0; k < K; ++k) {
+        int64_t r0, r1;
+        oracle_chunk_range(M, C, k, &r0, &r1);
+        /* LM head over the slice idx[r0..r1); its rows land at rows r0.. of out. */
+        int64_t total = (r1 - r0) * V;
+        double *chunk_out = out + r0 * V;
+#pragma omp parallel for schedule(static)
+        for (int64_t e = 0; e < total; ++e) {
+            int64_t r = r0 + e / V, v = e % V;
+            chunk_out[e] = lm_head_dot_bf16(H + (int64_t)idx[r] * d, W + v * d, d);
+        }
+    }
+    return 0;
+}
+
+/* Number of OpenMP threads the logits loops run on (1 when built without OpenMP). */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_num_threads(void) { return 1; }
+#endif
+
+/* Bytes of a logits tensor of `rows` rows over a vocabulary of V entries with
+ * `esize`-byte elements: rows * V * esize ("扩散大语言模型内存优化：从理论到系统设计",
+ * §2.2, where the dense [B, L, V] logits of a batch are sized this way).  Returns -1
+ * on overflow of a signed 64-bit count. */
+int64_t oracle_logits_bytes(int64_t rows, int64_t V, int64_t esize)
+{
+    if (rows < 0 || V < 0 || esize <= 0)
+        return -1;
+    if (rows != 0 && V > INT64_MAX / rows)
+        return -1;
+    int64_t n = rows * V;
+    if (n != 0 && esize > INT64_MAX / n)
+        return -1;
+    return n * esize;
+}
