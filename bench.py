@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Benchmark of the mask-only logits hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input, inputs
+already resident in HBM: stream compaction of the token ids into idx (one launch),
+read-back of the masked count M, then the fused gather-GEMM logits in row chunks of
+max_num_logits rows (one launch per chunk).
+
+Default workload: the logits-dominant long-context case -- L = 32768, d = 4096,
+V = 126464 (LLaDA-8B's vocabulary), mask ratio 0.9 (M = 29491), 4096-row chunks,
+bf16 inputs and logits, fp32 accumulation.  Prints ONE JSON line on stdout; details
+go to stderr.
+
+  value        whole-step TFLOP/s, counting 2*M*d*V per step
+  roofline     the gather-GEMM kernel against the dense bf16 MFMA peak (2.5 PFLOP/s):
+               achieved = (2*M*d*V of one step) / (GEMM time of one step), with the GEMM
+               time measured by HIP events on the stream the kernels run on
+  cpu_baseline the CPU oracle (fp64, OpenMP) timed on a bounded sample of rows
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "mask-only logits TFLOP/s (2·M·d·V) and % bf16 MFMA peak at L=32k, d=4096"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gather_gemm.hip", "mosaic_abi.cpp"):
+        with open(os.path.join(ROOT, "mask_only_logits_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gather_gemm_{workload}.json")
+    try:
+        with open(path, encoding="utf-8") as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, idx_np, target_s: float):
+    """Time the oracle on a bounded sample of masked rows (the first rows of idx)."""
+    import oracle
+    cores = oracle.num_threads()
+    flop_row = 2.0 * wl.d * wl.V
+    t0 = time.perf_counter()
+    oracle.masked_logits(wl.H, idx_np, wl.W, rows=list(range(2)))
+    t_cal = max(1e-3, time.perf_counter() - t0) / 2
+    n = int(max(2, min(len(idx_np), target_s / t_cal)))
+    rows = list(range(n))
+    t0 = time.perf_counter()
+    oracle.masked_logits(wl.H, idx_np, wl.W, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": round(n * flop_row / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {len(idx_np)} masked rows x all {wl.V} vocabulary rows of the same workload "
+                      f"(fp64, ascending k), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_logits")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path is a single-GPU kernel library); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mask_only_logits_amd import inputs
+    from mask_only_logits_amd import mosaic
+
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    wl = inputs.make_workload(args.workload)
+    log(f"[bench] inputs {args.workload}: L={wl.L} d={wl.d} V={wl.V} in {time.perf_counter() - t0:.1f}s")
+    tokens = wl.tokens.to(dev)
+    H = wl.H.to(dev)
+    W = wl.W.to(dev)
+    seq_offsets = wl.seq_offsets.to(dev) if wl.seq_offsets is not None else None
+    out_dtype = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
+    L, d, V = wl.L, wl.d, wl.V
+    idx = torch.empty(L, dtype=torch.int32, device=dev)
+    cnt = torch.empty(max(2, wl.nseq + 1), dtype=torch.int32, device=dev)
+
+    stream = torch.cuda.current_stream()
+
+    # Count once to size the output; every step recomputes it.
+    if seq_offsets is not None:
+        mosaic.mosaic_mask_compact_batched(tokens, seq_offsets, wl.mask_id, idx=idx, idx_offsets=cnt[: wl.nseq + 1])
+        M = int(cnt[wl.nseq].item())
+    else:
+        mosaic.mosaic_mask_compact(tokens, wl.mask_id, idx=idx, count=cnt[:1])
+        M = int(cnt[0].item())
+    out = torch.empty((M, V), dtype=out_dtype, device=dev)
+    C = wl.chunk_rows
+    launches = mosaic.mosaic_num_chunks(M, C)
+    flop = 2.0 * M * d * V
+    log(f"[bench] M={M} chunk_rows={C} launches={launches} variant="
+        f"{mosaic.mosaic_logits_variant(M, V, d, H.dtype, out_dtype)} out={out.numel() * out.element_size() / 1e9:.2f} GB")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(i=None):
+        if i is not None:
+            ev[i][0].record(stream)
+        if seq_offsets is not None:
+            mosaic.mosaic_mask_compact_batched(tokens, seq_offsets, wl.mask_id, idx=idx,
+                                               idx_offsets=cnt[: wl.nseq + 1], stream=stream)
+            m = int(cnt[wl.nseq].item())      # device -> host: sizes the GEMM
+        else:
+            mosaic.mosaic_mask_compact(tokens, wl.mask_id, idx=idx, count=cnt[:1], stream=stream)
+            m = int(cnt[0].item())
+        if i is not None:
+            ev[i][1].record(stream)
+        mosaic.mosaic_masked_logits(H, idx, W, M=m, out=out, chunk_rows=C, stream=stream)
+        if i is not None:
+            ev[i][2].record(stream)
+        return m
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        assert step(i) == M
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    gemm_ms = [a[1].elapsed_time(a[2]) for a in ev]
+    compact_ms = [a[0].elapsed_time(a[1]) for a in ev]
+    gemm_avg = float(np.mean(gemm_ms))
+    value = flop / (ms_per_step / 1e3) / 1e12
+    achieved = flop / (gemm_avg / 1e3) / 1e12
+    log(f"[bench] {ms_per_step:.3f} ms/step ({value:.1f} TFLOP/s); GEMM {gemm_avg:.3f} ms/step "
+        f"(min {min(gemm_ms):.3f}) = {achieved:.1f} TFLOP/s = {achieved / PEAK_BF16_TFLOPS:.1%} of bf16 peak; "
+        f"{gemm_avg / launches:.3f} ms per launch; compaction+readback {np.mean(compact_ms) * 1e3:.1f} us")
+
+    alg_bytes = launches * V * d * 2 + M * d * 2 + M * V * out.element_size() + M * 4
+    traffic = measured_traffic(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Gaussian H ~ N(0,1), W ~ N(0,0.02); uniform masked positions)",
+        "config": {"workload": args.workload, "L": L, "d": d, "V": V, "M": M, "chunk_rows": C,
+                   "launches_per_step": launches, "in_dtype": wl.dtype, "out_dtype": wl.out_dtype,
+                   "accumulate": "fp32"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "gather_gemm_bf16_kernel", "launch_ms_avg": round(gemm_avg / launches, 4),
+                     "algorithmic_bytes_per_launch": int(alg_bytes / launches),
+                     "hbm_frac_algorithmic": round(alg_bytes / (gemm_avg / 1e3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "detail": {"gemm_ms_per_step": round(gemm_avg, 4), "gemm_ms_min": round(min(gemm_ms), 4),
+                   "compaction_readback_us": round(float(np.mean(compact_ms)) * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        idx_np = idx[:M].cpu().numpy()
+        log("[bench] timing the CPU oracle on a row sample ...")
+        result["cpu_baseline"] = cpu_baseline(wl, idx_np, args.cpu_seconds)
+        log(f"[bench] cpu_baseline {result['cpu_baseline']}")
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

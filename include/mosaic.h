@@ -1,0 +1,149 @@
+/*
+ * mosaic.h -- C ABI of the mask-only logits hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The path has three steps, each an entry point below:
+ *
+ *   1. compaction   mask (token ids or flags) -> ascending list idx[M] of masked rows;
+ *   2. logits       logits[M, V] = H[idx, :] . W^T, a gather fused into the GEMM: the
+ *                   masked rows are read from the full hidden states through idx and
+ *                   no gathered copy of H is ever written;
+ *   3. chunking     step 2 in consecutive row slices of at most max_num_logits rows.
+ *
+ * Sources (web pages on Mosaic, a diffusion-LLM memory system):
+ *   [MR]  "Mosaic: Unlocking Long-Context Inference for Diffusion LLMs via Global
+ *         Memory" (paper review, xllm-io.github.io), 核心观察 #2 (logits over unmasked
+ *         tokens are wasted work; only masked tokens are sampled) and 核心组件
+ *         "1. Mask-only Logits Kernel" (the kernel takes all tokens' hidden states and
+ *         the mask indices, tiles the work over the compute units, addresses rows
+ *         indirectly through the indices, needs no intermediate buffer, runs as one
+ *         launch).
+ *   [MP]  "扩散大语言模型内存优化：Mosaic系统突破与实践" (jsqmd.com), §2.2 (gather-GEMM
+ *         fusion: indirect addressing through the mask index into the original hidden
+ *         states; tiles over compute units; on-chip staging, no global temporary).
+ *   [DS]  "扩散大语言模型内存优化：从理论到系统设计" (cnnetsun.cn), §3.2.2 (when more
+ *         rows need logits than max_num_logits, process them in micro-batches of at most
+ *         max_num_logits rows and concatenate the results in order) and §2.2 (the
+ *         logits tensor of a batch is rows x V elements).
+ *   [MA]  Mosaic abstract (zhuanzhiai.com): the system preserves exact model outputs,
+ *         i.e. the mask-only rows equal the dense logits' rows.
+ *
+ * Conventions shared by every entry point
+ *   - Every array pointer is a DEVICE pointer owned by the caller.  The library never
+ *     allocates, frees or synchronises; all work is enqueued on `stream` (a
+ *     hipStream_t passed as void*, NULL = the null stream) and is asynchronous.
+ *   - Every function returns a status and prints nothing.  All argument validation
+ *     happens before anything is enqueued; on INVALID_ARG or UNSUPPORTED no output
+ *     is touched.  MOSAIC_ERR_DEVICE means a launch failed (earlier chunks of a
+ *     chunked call may already be written; rerunning the call rewrites them).
+ *   - Calls on different streams are independent; the library holds no state.
+ *   - Sizes are int64_t; positions and row ids are int32_t (so L < 2^31).
+ */
+#ifndef MOSAIC_H
+#define MOSAIC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOSAIC_OK = 0,
+    MOSAIC_ERR_INVALID_ARG = 1,   /* null pointer, negative size, misalignment, overflow */
+    MOSAIC_ERR_UNSUPPORTED = 2,   /* valid but not supported: dtype pair, d not a multiple of 8 */
+    MOSAIC_ERR_DEVICE = 3         /* a HIP launch failed */
+} mosaic_status_t;
+
+typedef enum {
+    MOSAIC_F32 = 0,               /* IEEE binary32 */
+    MOSAIC_BF16 = 1               /* bfloat16 (upper half of binary32) */
+} mosaic_dtype_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *mosaic_status_string(mosaic_status_t s);
+
+/* ---------------------------------------------------------------- compaction --- */
+
+/* Step 1 for one sequence ([MR] 核心组件 1 takes "the mask indices" as an input; [MP]
+ * §2.2 addresses rows through them).
+ *   tokens  int32[L]  token ids; position p is masked when tokens[p] == mask_id.
+ *   idx     int32[L]  capacity L; on return idx[0..M) = the masked positions in
+ *                     ascending order (entries from M on are left untouched).
+ *   count   int32[1]  on return M.
+ * L == 0 writes count = 0.  L >= 2^31 -> UNSUPPORTED.  Null tokens/idx with L > 0,
+ * null count, or L < 0 -> INVALID_ARG.  Runs as a single workgroup (one launch). */
+mosaic_status_t mosaic_mask_compact(const int32_t *tokens, int64_t L, int32_t mask_id,
+                                    int32_t *idx, int32_t *count, void *stream);
+
+/* Same as mosaic_mask_compact with a flag array: position p is masked when
+ * flags[p] != 0.  flags is uint8[L]. */
+mosaic_status_t mosaic_mask_compact_flags(const uint8_t *flags, int64_t L,
+                                          int32_t *idx, int32_t *count, void *stream);
+
+/* Step 1 for a ragged batch of nseq sequences concatenated into tokens[L].
+ *   seq_offsets  int32[nseq+1]  sequence s owns positions [seq_offsets[s], seq_offsets[s+1]);
+ *                               the caller guarantees seq_offsets[0] = 0, nondecreasing,
+ *                               seq_offsets[nseq] = L (not checked on the device).
+ *   idx          int32[L]       on return the masked GLOBAL positions, sequence by
+ *                               sequence, ascending within each (so ascending overall).
+ *   idx_offsets  int32[nseq+1]  on return CSR offsets: sequence s's masked rows are
+ *                               idx[idx_offsets[s] .. idx_offsets[s+1]); idx_offsets[nseq] = M.
+ * nseq <= 0 -> INVALID_ARG.  Two launches (compaction, then the CSR offsets). */
+mosaic_status_t mosaic_mask_compact_batched(const int32_t *tokens, int64_t L,
+                                            const int32_t *seq_offsets, int32_t nseq,
+                                            int32_t mask_id, int32_t *idx, int32_t *idx_offsets,
+                                            void *stream);
+
+/* ------------------------------------------------------------------- logits --- */
+
+/* Steps 2 and 3: out[i, v] = sum_k H[idx[i], k] * W[v, k] for i < M, v < V
+ * ([MR] 核心观察 #2 and 核心组件 1; [MP] §2.2), computed in row chunks of at most
+ * chunk_rows rows, one kernel launch per chunk, written in order ([DS] §3.2.2).
+ *   H      [L, d] row-major, in_dtype   final hidden states of ALL L positions.
+ *   idx    int32[M]                     rows of H to use, each in [0, L); any order,
+ *                                       repeats allowed.  Out-of-range values are a
+ *                                       contract violation (undefined behaviour).
+ *   W      [V, d] row-major, in_dtype   LM-head weight (K-contiguous rows).
+ *   out    [M, V] row-major, out_dtype  row i holds the logits of position idx[i].
+ *   chunk_rows  max_num_logits: <= 0 or >= M runs one chunk; otherwise
+ *               ceil(M / chunk_rows) chunks [k*C, min(M, (k+1)*C)).  The kernel
+ *               variant is chosen once per call from M, so every chunk of a call
+ *               uses the same one and the output is bit-identical for every
+ *               chunk_rows value.
+ * Dtype pairs (in -> out): F32->F32, BF16->BF16, BF16->F32.  Products are
+ * accumulated in fp32 (bf16 MFMA with fp32 accumulators; fp32 FMA for F32 inputs);
+ * bf16 outputs are rounded to nearest even.
+ * Requirements: d % 8 == 0 (BF16) or d % 4 == 0 (F32), else UNSUPPORTED; H, W and
+ * out 16-byte aligned, else INVALID_ARG; M * V * esize must fit in int64.
+ * M == 0 or V == 0: MOSAIC_OK and nothing is enqueued (pointers may be NULL).
+ * Streaming use ([DS] §3.2.3, free each micro-batch early): call once per chunk with
+ * idx + k*C, M = rows of chunk k, chunk_rows = 0 and a reused [C, V] buffer. */
+mosaic_status_t mosaic_masked_logits(const void *H, int64_t L, int64_t d,
+                                     const int32_t *idx, int64_t M,
+                                     const void *W, int64_t V,
+                                     void *out, int64_t chunk_rows,
+                                     mosaic_dtype_t in_dtype, mosaic_dtype_t out_dtype,
+                                     void *stream);
+
+/* ------------------------------------------------------------ host helpers --- */
+
+/* Number of chunks a call of mosaic_masked_logits makes for M rows ([DS] §3.2.2):
+ * 0 for M <= 0, 1 for chunk_rows <= 0 or chunk_rows >= M, else ceil(M / chunk_rows). */
+int64_t mosaic_num_chunks(int64_t M, int64_t chunk_rows);
+
+/* Bytes of a logits tensor of `rows` rows over V vocabulary entries of dtype `dt`
+ * ([DS] §2.2): rows * V * esize, written to *bytes.  INVALID_ARG on a negative size,
+ * an unknown dtype, a NULL `bytes` or overflow of int64. */
+mosaic_status_t mosaic_logits_bytes(int64_t rows, int64_t V, mosaic_dtype_t dt, int64_t *bytes);
+
+/* Which kernel variant mosaic_masked_logits runs for M rows of this dtype pair
+ * (a stable small integer, for tests and profiles), or -1 if unsupported. */
+int mosaic_logits_variant(int64_t M, int64_t V, int64_t d, mosaic_dtype_t in_dtype,
+                          mosaic_dtype_t out_dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOSAIC_H */

@@ -1,0 +1,31 @@
+// Internal launchers of the HIP kernels (not part of the public C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mosaic {
+
+hipError_t launch_mask_compact(const int32_t *tokens, int64_t L, int32_t mask_id, int32_t *idx,
+                               int32_t *count, hipStream_t stream);
+hipError_t launch_mask_compact_flags(const uint8_t *flags, int64_t L, int32_t *idx, int32_t *count,
+                                     hipStream_t stream);
+hipError_t launch_mask_compact_batched(const int32_t *tokens, int64_t L, const int32_t *seq_offsets,
+                                       int32_t nseq, int32_t mask_id, int32_t *idx,
+                                       int32_t *idx_offsets, hipStream_t stream);
+
+// Kernel variants of the logits GEMM.
+enum LogitsVariant : int {
+    kVariantF32 = 0,          // fp32 inputs: LDS-tiled FMA kernel
+    kVariantBf16Tile256 = 1,  // bf16 inputs, d % 64 == 0: 256 x 256 MFMA tile, 2-stage LDS pipeline
+    kVariantBf16Simple = 2,   // bf16 inputs, any d % 8 == 0: LDS-tiled FMA kernel
+};
+
+// Whether a chunk of `rows` rows over V vocabulary rows fits the variant's launch grid.
+bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V);
+
+// One chunk: out[i, v] for i < rows, v < V, out row stride ldo elements.
+hipError_t launch_gather_gemm(int variant, const void *H, const int32_t *idx, int64_t rows,
+                              const void *W, int64_t V, int64_t d, void *out, int64_t ldo,
+                              bool out_bf16, hipStream_t stream);
+
+}  // namespace mosaic

@@ -1,0 +1,174 @@
+// C ABI of the mask-only logits path (declared in include/mosaic.h): argument
+// validation, kernel-variant choice and the row-chunk driver.
+//
+// The chunk driver follows dLLM-Serve's logit budget ("扩散大语言模型内存优化：从理论到
+// 系统设计", §3.2.2): when more rows need logits than max_num_logits, the rows are
+// processed in consecutive micro-batches of at most max_num_logits rows whose outputs
+// land, in order, in consecutive row ranges of `out`.  Each chunk is one launch of the
+// fused gather-GEMM, which reads its rows of H through its slice of idx.
+//
+// Validation happens entirely on the host, before any HIP call, so a rejected call
+// touches neither the device nor `out`.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mosaic.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxPos = 0x7fffffffLL;   // positions and rows are int32
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t esize_of(mosaic_dtype_t t) { return t == MOSAIC_F32 ? 4 : (t == MOSAIC_BF16 ? 2 : 0); }
+
+// M * V * esize without int64 overflow; -1 on overflow.
+int64_t checked_bytes(int64_t rows, int64_t V, int64_t esize)
+{
+    if (rows < 0 || V < 0 || esize <= 0)
+        return -1;
+    if (rows != 0 && V > INT64_MAX / rows)
+        return -1;
+    const int64_t n = rows * V;
+    if (n != 0 && esize > INT64_MAX / n)
+        return -1;
+    return n * esize;
+}
+
+int pick_variant(int64_t M, int64_t V, int64_t d, mosaic_dtype_t in, mosaic_dtype_t out)
+{
+    (void)M;
+    (void)V;
+    if (in == MOSAIC_F32 && out == MOSAIC_F32)
+        return d % 4 == 0 ? mosaic::kVariantF32 : -1;
+    if (in == MOSAIC_BF16 && (out == MOSAIC_BF16 || out == MOSAIC_F32)) {
+        if (d % 8 != 0)
+            return -1;
+        // The tiled kernel addresses a 256-row W slab with 32-bit byte offsets.
+        return (d % 64 == 0 && d <= (1 << 22)) ? mosaic::kVariantBf16Tile256 : mosaic::kVariantBf16Simple;
+    }
+    return -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mosaic_status_string(mosaic_status_t s)
+{
+    switch (s) {
+    case MOSAIC_OK: return "MOSAIC_OK";
+    case MOSAIC_ERR_INVALID_ARG: return "MOSAIC_ERR_INVALID_ARG";
+    case MOSAIC_ERR_UNSUPPORTED: return "MOSAIC_ERR_UNSUPPORTED";
+    case MOSAIC_ERR_DEVICE: return "MOSAIC_ERR_DEVICE";
+    }
+    return "MOSAIC_ERR_UNKNOWN";
+}
+
+int64_t mosaic_num_chunks(int64_t M, int64_t chunk_rows)
+{
+    if (M <= 0)
+        return 0;
+    if (chunk_rows <= 0 || chunk_rows >= M)
+        return 1;
+    return (M + chunk_rows - 1) / chunk_rows;
+}
+
+mosaic_status_t mosaic_logits_bytes(int64_t rows, int64_t V, mosaic_dtype_t dt, int64_t *bytes)
+{
+    const int64_t es = esize_of(dt);
+    if (!bytes || es == 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    const int64_t n = checked_bytes(rows, V, es);
+    if (n < 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    *bytes = n;
+    return MOSAIC_OK;
+}
+
+int mosaic_logits_variant(int64_t M, int64_t V, int64_t d, mosaic_dtype_t in_dtype, mosaic_dtype_t out_dtype)
+{
+    return pick_variant(M, V, d, in_dtype, out_dtype);
+}
+
+mosaic_status_t mosaic_mask_compact(const int32_t *tokens, int64_t L, int32_t mask_id, int32_t *idx,
+                                    int32_t *count, void *stream)
+{
+    if (L < 0 || !count || (L > 0 && (!tokens || !idx)))
+        return MOSAIC_ERR_INVALID_ARG;
+    if (L > kMaxPos)
+        return MOSAIC_ERR_UNSUPPORTED;
+    return mosaic::launch_mask_compact(tokens, L, mask_id, idx, count, (hipStream_t)stream) == hipSuccess
+               ? MOSAIC_OK
+               : MOSAIC_ERR_DEVICE;
+}
+
+mosaic_status_t mosaic_mask_compact_flags(const uint8_t *flags, int64_t L, int32_t *idx, int32_t *count,
+                                          void *stream)
+{
+    if (L < 0 || !count || (L > 0 && (!flags || !idx)))
+        return MOSAIC_ERR_INVALID_ARG;
+    if (L > kMaxPos)
+        return MOSAIC_ERR_UNSUPPORTED;
+    return mosaic::launch_mask_compact_flags(flags, L, idx, count, (hipStream_t)stream) == hipSuccess
+               ? MOSAIC_OK
+               : MOSAIC_ERR_DEVICE;
+}
+
+mosaic_status_t mosaic_mask_compact_batched(const int32_t *tokens, int64_t L, const int32_t *seq_offsets,
+                                            int32_t nseq, int32_t mask_id, int32_t *idx,
+                                            int32_t *idx_offsets, void *stream)
+{
+    if (L < 0 || nseq <= 0 || !seq_offsets || !idx_offsets || (L > 0 && (!tokens || !idx)))
+        return MOSAIC_ERR_INVALID_ARG;
+    if (L > kMaxPos)
+        return MOSAIC_ERR_UNSUPPORTED;
+    return mosaic::launch_mask_compact_batched(tokens, L, seq_offsets, nseq, mask_id, idx, idx_offsets,
+                                               (hipStream_t)stream) == hipSuccess
+               ? MOSAIC_OK
+               : MOSAIC_ERR_DEVICE;
+}
+
+mosaic_status_t mosaic_masked_logits(const void *H, int64_t L, int64_t d, const int32_t *idx, int64_t M,
+                                     const void *W, int64_t V, void *out, int64_t chunk_rows,
+                                     mosaic_dtype_t in_dtype, mosaic_dtype_t out_dtype, void *stream)
+{
+    if (M < 0 || V < 0 || L < 0 || d < 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    const int64_t in_es = esize_of(in_dtype), out_es = esize_of(out_dtype);
+    if (in_es == 0 || out_es == 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (M == 0 || V == 0)
+        return MOSAIC_OK;   // no rows or no vocabulary: nothing to compute
+    if (!H || !W || !idx || !out || L == 0 || d == 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (!aligned16(H) || !aligned16(W) || !aligned16(out) || ((uintptr_t)idx & 3u))
+        return MOSAIC_ERR_INVALID_ARG;
+    if (checked_bytes(M, V, out_es) < 0 || checked_bytes(L, d, in_es) < 0 || checked_bytes(V, d, in_es) < 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (L > kMaxPos || V > kMaxPos || d > kMaxPos)
+        return MOSAIC_ERR_UNSUPPORTED;
+    const int variant = pick_variant(M, V, d, in_dtype, out_dtype);
+    if (variant < 0)
+        return MOSAIC_ERR_UNSUPPORTED;
+
+    // Row chunks ([k*C, min(M, (k+1)*C))), one launch each, same variant for all.
+    const int64_t K = mosaic_num_chunks(M, chunk_rows);
+    const int64_t C = (K == 1) ? M : chunk_rows;
+    if (C > kMaxPos || !mosaic::gather_gemm_grid_fits(variant, C, V))
+        return MOSAIC_ERR_UNSUPPORTED;
+    const bool out_bf16 = out_dtype == MOSAIC_BF16;
+    for (int64_t k = 0; k < K; ++k) {
+        const int64_t r0 = k * C;
+        const int64_t r1 = (r0 + C < M) ? r0 + C : M;
+        void *chunk_out = (char *)out + r0 * V * out_es;
+        const hipError_t e = mosaic::launch_gather_gemm(variant, H, idx + r0, r1 - r0, W, V, d, chunk_out, V,
+                                                        out_bf16, (hipStream_t)stream);
+        if (e != hipSuccess)
+            return MOSAIC_ERR_DEVICE;
+    }
+    return MOSAIC_OK;
+}
+
+}  // extern "C"

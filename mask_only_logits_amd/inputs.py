@@ -214,7 +214,7 @@ def make_random(seed: int, L: int, d: int, V: int, M: int, *, dtype: str = "bf16
     s_mask, s_tok, s_h, s_w = ss.spawn(4)
     rm = np.random.Generator(np.random.PCG64(s_mask))
     rt = np.random.Generator(np.random.PCG64(s_tok))
-    mask_id = V - 1
+    mask_id = max(V - 1, 1)
     positions = scattered_positions(rm, L, M)
     tokens = torch.from_numpy(mask_tokens(rt, L, positions, mask_id))
     H = to_dtype(gaussian((L, d), 1.0, s_h), dtype)

@@ -1,0 +1,203 @@
+"""Thin Python binding of libmosaic.so (include/mosaic.h).
+
+Each function has the name of the C entry point it calls and only marshals
+arguments: torch tensors become device pointers, the current torch stream becomes
+the hipStream_t, and a non-OK status becomes an exception.  Every step of the
+path runs in the HIP kernels; there is no fallback.  If the library is missing the
+import fails with an error that says how to build it.
+
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+_LIB_PATH = Path(__file__).resolve().parent / "libmosaic.so"
+
+MOSAIC_OK = 0
+MOSAIC_ERR_INVALID_ARG = 1
+MOSAIC_ERR_UNSUPPORTED = 2
+MOSAIC_ERR_DEVICE = 3
+MOSAIC_F32 = 0
+MOSAIC_BF16 = 1
+
+# Every symbol include/mosaic.h declares.
+EXPORTS = (
+    "mosaic_status_string",
+    "mosaic_mask_compact",
+    "mosaic_mask_compact_flags",
+    "mosaic_mask_compact_batched",
+    "mosaic_masked_logits",
+    "mosaic_num_chunks",
+    "mosaic_logits_bytes",
+    "mosaic_logits_variant",
+)
+
+
+class MosaicError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {mosaic_status_string(status)} ({status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not _LIB_PATH.exists():
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m mask_only_logits_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    i64, i32, p, st = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int
+    lib.mosaic_status_string.restype = ctypes.c_char_p
+    lib.mosaic_status_string.argtypes = [st]
+    lib.mosaic_mask_compact.restype = st
+    lib.mosaic_mask_compact.argtypes = [p, i64, i32, p, p, p]
+    lib.mosaic_mask_compact_flags.restype = st
+    lib.mosaic_mask_compact_flags.argtypes = [p, i64, p, p, p]
+    lib.mosaic_mask_compact_batched.restype = st
+    lib.mosaic_mask_compact_batched.argtypes = [p, i64, p, i32, i32, p, p, p]
+    lib.mosaic_masked_logits.restype = st
+    lib.mosaic_masked_logits.argtypes = [p, i64, i64, p, i64, p, i64, p, i64, st, st, p]
+    lib.mosaic_num_chunks.restype = i64
+    lib.mosaic_num_chunks.argtypes = [i64, i64]
+    lib.mosaic_logits_bytes.restype = st
+    lib.mosaic_logits_bytes.argtypes = [i64, i64, st, ctypes.POINTER(i64)]
+    lib.mosaic_logits_variant.restype = ctypes.c_int
+    lib.mosaic_logits_variant.argtypes = [i64, i64, i64, st, st]
+    return lib
+
+
+lib = _load()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return MOSAIC_F32
+    if t == torch.bfloat16:
+        return MOSAIC_BF16
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _torch_dtype(code: int) -> torch.dtype:
+    return {MOSAIC_F32: torch.float32, MOSAIC_BF16: torch.bfloat16}[code]
+
+
+def _dev(t: torch.Tensor | None, name: str, dtype: torch.dtype | None = None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int, where: str):
+    if status != MOSAIC_OK:
+        raise MosaicError(status, where)
+
+
+def mosaic_status_string(status: int) -> str:
+    return lib.mosaic_status_string(int(status)).decode()
+
+
+def mosaic_num_chunks(M: int, chunk_rows: int) -> int:
+    return int(lib.mosaic_num_chunks(int(M), int(chunk_rows)))
+
+
+def mosaic_logits_bytes(rows: int, V: int, dtype: torch.dtype) -> int:
+    out = ctypes.c_int64()
+    _check(lib.mosaic_logits_bytes(int(rows), int(V), _dtype_code(dtype), ctypes.byref(out)),
+           "mosaic_logits_bytes")
+    return int(out.value)
+
+
+def mosaic_logits_variant(M: int, V: int, d: int, in_dtype: torch.dtype, out_dtype: torch.dtype) -> int:
+    return int(lib.mosaic_logits_variant(int(M), int(V), int(d), _dtype_code(in_dtype), _dtype_code(out_dtype)))
+
+
+def mosaic_mask_compact(tokens: torch.Tensor, mask_id: int, idx: torch.Tensor | None = None,
+                        count: torch.Tensor | None = None, stream=None):
+    """Masked positions of int32 `tokens` in ascending order -> (idx [L] int32, count [1] int32).
+
+    Asynchronous: idx[:count] holds the list once the stream reaches this point."""
+    L = tokens.numel()
+    if idx is None:
+        idx = torch.empty(max(L, 1), dtype=torch.int32, device=tokens.device)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=tokens.device)
+    _check(lib.mosaic_mask_compact(_dev(tokens, "tokens", torch.int32), L, int(mask_id),
+                                   _dev(idx, "idx", torch.int32), _dev(count, "count", torch.int32),
+                                   _stream(stream)), "mosaic_mask_compact")
+    return idx, count
+
+
+def mosaic_mask_compact_flags(flags: torch.Tensor, idx: torch.Tensor | None = None,
+                              count: torch.Tensor | None = None, stream=None):
+    """Positions with flags != 0 (uint8 or bool flags) -> (idx, count)."""
+    if flags.dtype == torch.bool:
+        flags = flags.view(torch.uint8)
+    L = flags.numel()
+    if idx is None:
+        idx = torch.empty(max(L, 1), dtype=torch.int32, device=flags.device)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=flags.device)
+    _check(lib.mosaic_mask_compact_flags(_dev(flags, "flags", torch.uint8), L, _dev(idx, "idx", torch.int32),
+                                         _dev(count, "count", torch.int32), _stream(stream)),
+           "mosaic_mask_compact_flags")
+    return idx, count
+
+
+def mosaic_mask_compact_batched(tokens: torch.Tensor, seq_offsets: torch.Tensor, mask_id: int,
+                                idx: torch.Tensor | None = None, idx_offsets: torch.Tensor | None = None,
+                                stream=None):
+    """Ragged batch -> (idx [L] global positions, idx_offsets [nseq+1] CSR)."""
+    L = tokens.numel()
+    nseq = seq_offsets.numel() - 1
+    if idx is None:
+        idx = torch.empty(max(L, 1), dtype=torch.int32, device=tokens.device)
+    if idx_offsets is None:
+        idx_offsets = torch.empty(max(nseq + 1, 1), dtype=torch.int32, device=tokens.device)
+    _check(lib.mosaic_mask_compact_batched(_dev(tokens, "tokens", torch.int32), L,
+                                           _dev(seq_offsets, "seq_offsets", torch.int32), nseq, int(mask_id),
+                                           _dev(idx, "idx", torch.int32),
+                                           _dev(idx_offsets, "idx_offsets", torch.int32), _stream(stream)),
+           "mosaic_mask_compact_batched")
+    return idx, idx_offsets
+
+
+def mosaic_masked_logits(H: torch.Tensor, idx: torch.Tensor, W: torch.Tensor, M: int | None = None,
+                         out: torch.Tensor | None = None, chunk_rows: int = 0,
+                         out_dtype: torch.dtype | None = None, stream=None) -> torch.Tensor:
+    """logits[M, V] = H[idx[:M], :] @ W.T in chunks of at most chunk_rows rows.
+
+    H [L, d] and W [V, d] share a dtype (bf16 or fp32); idx is int32 with at least M
+    entries (M defaults to idx.numel()).  `out` (allocated if absent) is [M, V]."""
+    if H.dim() != 2 or W.dim() != 2 or H.shape[1] != W.shape[1]:
+        raise ValueError("H must be [L, d] and W [V, d]")
+    if H.dtype != W.dtype:
+        raise TypeError("H and W must share a dtype")
+    L, d = H.shape
+    V = W.shape[0]
+    M = idx.numel() if M is None else int(M)
+    if M > idx.numel():
+        raise ValueError("M exceeds the length of idx")
+    if out is None:
+        out = torch.empty((M, V), dtype=out_dtype or H.dtype, device=H.device)
+    elif out.numel() < M * V:
+        raise ValueError("out is smaller than M * V")
+    _check(lib.mosaic_masked_logits(_dev(H, "H"), L, d, _dev(idx, "idx", torch.int32), M, _dev(W, "W"), V,
+                                    _dev(out, "out"), int(chunk_rows), _dtype_code(H.dtype),
+                                    _dtype_code(out.dtype), _stream(stream)), "mosaic_masked_logits")
+    return out

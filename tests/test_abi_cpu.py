@@ -1,0 +1,125 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, and its
+host-side logic (status strings, chunk arithmetic, size helper, argument validation)
+behaves as declared.  No call here enqueues device work: every call is rejected by
+validation before any HIP call, or returns early for empty problems."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    from mask_only_logits_amd import mosaic
+    return mosaic
+
+
+def test_exports_every_declared_symbol(m):
+    hdr = open(os.path.join(ROOT, "include", "mosaic.h"), encoding="utf-8").read()
+    declared = set(re.findall(r"\b(mosaic_[a-z_]+)\s*\(", hdr))
+    assert declared == set(m.EXPORTS)
+    for name in declared:
+        assert hasattr(m.lib, name), name
+
+
+def test_status_strings(m):
+    assert m.mosaic_status_string(0) == "MOSAIC_OK"
+    assert m.mosaic_status_string(1) == "MOSAIC_ERR_INVALID_ARG"
+    assert m.mosaic_status_string(2) == "MOSAIC_ERR_UNSUPPORTED"
+    assert m.mosaic_status_string(3) == "MOSAIC_ERR_DEVICE"
+    assert m.mosaic_status_string(99) == "MOSAIC_ERR_UNKNOWN"
+
+
+def test_num_chunks_matches_oracle(m):
+    for M in list(range(0, 70)) + [1229, 29491, 39322]:
+        for C in (-2, 0, 1, 2, 7, 63, 64, 65, 4096, 8192):
+            assert m.mosaic_num_chunks(M, C) == oracle.num_chunks(M, C), (M, C)
+
+
+def test_logits_bytes(m):
+    import torch
+    assert m.mosaic_logits_bytes(16 * 2048, 126464, torch.bfloat16) == 8_287_944_704
+    assert m.mosaic_logits_bytes(29491, 126464, torch.bfloat16) == 7_459_099_648
+    assert m.mosaic_logits_bytes(128, 1024, torch.float32) == 524_288
+    out = ctypes.c_int64(-7)
+    assert m.lib.mosaic_logits_bytes(2**62, 4, 1, ctypes.byref(out)) == m.MOSAIC_ERR_INVALID_ARG
+    assert m.lib.mosaic_logits_bytes(-1, 4, 1, ctypes.byref(out)) == m.MOSAIC_ERR_INVALID_ARG
+    assert m.lib.mosaic_logits_bytes(1, 4, 7, ctypes.byref(out)) == m.MOSAIC_ERR_INVALID_ARG
+    assert m.lib.mosaic_logits_bytes(1, 4, 1, None) == m.MOSAIC_ERR_INVALID_ARG
+    assert out.value == -7
+
+
+def test_variant_choice(m):
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    assert m.mosaic_logits_variant(29491, 126464, 4096, bf, bf) == 1
+    assert m.mosaic_logits_variant(20, 152064, 3584, bf, bf) == m.mosaic_logits_variant(20, 152064, 3584, bf, bf)
+    assert m.mosaic_logits_variant(128, 1024, 256, f32, f32) == 0
+    assert m.mosaic_logits_variant(10, 10, 72, bf, f32) == 2          # d % 64 != 0
+    assert m.mosaic_logits_variant(10, 10, 12, bf, bf) == -1          # d % 8 != 0
+    assert m.mosaic_logits_variant(10, 10, 64, f32, bf) == -1         # fp32 -> bf16 not offered
+
+
+# Fake, never-dereferenced addresses: validation rejects these calls before any HIP call.
+A16 = 1 << 20            # 16-byte aligned
+A8 = (1 << 20) + 8       # misaligned for 16 bytes
+
+
+def _logits(m, H=A16, L=100, d=64, idx=A16, M=10, W=A16, V=50, out=A16, C=0, i=1, o=1):
+    return m.lib.mosaic_masked_logits(H, L, d, idx, M, W, V, out, C, i, o, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), 1), (dict(V=-1), 1), (dict(L=-1), 1), (dict(d=-1), 1),
+    (dict(H=None), 1), (dict(W=None), 1), (dict(idx=None), 1), (dict(out=None), 1),
+    (dict(L=0), 1), (dict(d=0), 1),
+    (dict(H=A8), 1), (dict(W=A8), 1), (dict(out=A8), 1), (dict(idx=A16 + 2), 1),
+    (dict(i=5), 1), (dict(o=9), 1),
+    (dict(d=12), 2), (dict(i=0, o=1), 2), (dict(i=0, o=0, d=6), 2),
+    (dict(M=2**40, V=2**30), 1),
+    (dict(L=2**31), 2),
+])
+def test_logits_validation(m, kw, status):
+    assert _logits(m, **kw) == status
+
+
+def test_empty_problems_are_ok_without_pointers(m):
+    assert _logits(m, M=0, H=None, W=None, idx=None, out=None) == 0
+    assert _logits(m, V=0, H=None, W=None, idx=None, out=None) == 0
+
+
+def test_compact_validation(m):
+    L = m.lib
+    assert L.mosaic_mask_compact(A16, -1, 0, A16, A16, None) == 1
+    assert L.mosaic_mask_compact(None, 10, 0, A16, A16, None) == 1
+    assert L.mosaic_mask_compact(A16, 10, 0, None, A16, None) == 1
+    assert L.mosaic_mask_compact(A16, 10, 0, A16, None, None) == 1
+    assert L.mosaic_mask_compact(A16, 2**31, 0, A16, A16, None) == 2
+    assert L.mosaic_mask_compact_flags(None, 10, A16, A16, None) == 1
+    assert L.mosaic_mask_compact_flags(A16, 10, A16, None, None) == 1
+    assert L.mosaic_mask_compact_batched(A16, 10, A16, 0, 0, A16, A16, None) == 1
+    assert L.mosaic_mask_compact_batched(A16, 10, None, 2, 0, A16, A16, None) == 1
+    assert L.mosaic_mask_compact_batched(A16, 10, A16, 2, 0, A16, None, None) == 1
+    assert L.mosaic_mask_compact_batched(A16, 2**31, A16, 2, 0, A16, A16, None) == 2
+
+
+def test_binding_rejects_host_tensors(m):
+    import torch
+    with pytest.raises(ValueError):
+        m.mosaic_mask_compact(torch.zeros(4, dtype=torch.int32), 1,
+                              idx=torch.zeros(4, dtype=torch.int32), count=torch.zeros(1, dtype=torch.int32))
+
+
+def test_product_path_does_not_touch_the_oracle():
+    # the package's sources never import or load the CPU oracle
+    pkg = os.path.join(ROOT, "mask_only_logits_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in text and "liboracle" not in text, f

@@ -1,0 +1,121 @@
+"""GPU path on the named workloads at full size.
+
+Compaction is compared with the oracle bit for bit.  Logits are compared with the
+fp64 oracle on every element for the small workloads and on sampled rows (chunk and
+tile boundaries plus seeded random rows) for the large ones, in the same launch
+configuration the benchmark times (the workload's own chunk_rows).  Properties that
+hold at any size are checked on every element: chunked == unchunked bit for bit, and
+one-hot weights reproduce the gathered hidden-state columns exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mask_only_logits_amd import inputs
+from tests.helpers import assert_close, bf16_rne, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def m():
+    from mask_only_logits_amd import mosaic
+    return mosaic
+
+
+def _step(m, wl, chunk_rows=None):
+    """Compaction + count read-back + chunked logits, as the benchmark runs them."""
+    tok = wl.tokens.to(DEV)
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    if wl.seq_offsets is not None:
+        idx, off = m.mosaic_mask_compact_batched(tok, wl.seq_offsets.to(DEV), wl.mask_id)
+        M = int(off[-1].item())
+    else:
+        idx, cnt = m.mosaic_mask_compact(tok, wl.mask_id)
+        M = int(cnt.item())
+    C = wl.chunk_rows if chunk_rows is None else chunk_rows
+    out = m.mosaic_masked_logits(H, idx, W, M=M, chunk_rows=C,
+                                 out_dtype=torch.float32 if wl.out_dtype == "f32" else torch.bfloat16)
+    torch.cuda.synchronize()
+    return H, W, idx, M, out
+
+
+def test_tiny_full(m):
+    wl = inputs.make_workload("tiny")
+    _, _, idx, M, out = _step(m, wl)
+    want = oracle.mask_compact(wl.tokens, wl.mask_id)
+    assert M == 128 and np.array_equal(idx[:M].cpu().numpy(), want)
+    assert out.dtype == torch.float32
+    assert_close(out, oracle.masked_logits(wl.H, want, wl.W), "tiny")
+
+
+def test_lowm_full(m):
+    wl = inputs.make_workload("lowm")
+    _, _, idx, M, out = _step(m, wl)
+    want = oracle.mask_compact(wl.tokens, wl.mask_id)
+    assert M == 20 and np.array_equal(idx[:M].cpu().numpy(), want)
+    assert_close(out, oracle.masked_logits(wl.H, want, wl.W), "lowm")
+
+
+@pytest.mark.parametrize("name,n_random", [("llada_step", 16), ("long_logits", 8), ("long_ffn", 8)])
+def test_large_sampled_and_chunk_bit_exact(m, name, n_random):
+    wl = inputs.make_workload(name)
+    H, W, idx, M, out = _step(m, wl)
+    want = oracle.mask_compact(wl.tokens, wl.mask_id)
+    assert M == want.size and np.array_equal(idx[:M].cpu().numpy(), want)
+    rows = sample_rows(M, wl.chunk_rows, n_random, seed=M)
+    ref = oracle.masked_logits(wl.H, want, wl.W, rows=rows)
+    assert_close(out[torch.from_numpy(rows).to(DEV)], ref, f"{name} sampled rows")
+    # chunked (the workload's max_num_logits, or a forced 1000-row chunking) == unchunked
+    other = m.mosaic_masked_logits(H, idx, W, M=M, chunk_rows=0 if wl.chunk_rows else 1000)
+    torch.cuda.synchronize()
+    assert torch.equal(other, out)
+
+
+def test_ragged_full_batch(m):
+    wl = inputs.make_workload("ragged")
+    H, W, idx, M, out = _step(m, wl)
+    want_idx, want_off = oracle.mask_compact_batched(wl.tokens, wl.seq_offsets, wl.mask_id)
+    assert M == want_off[-1] and np.array_equal(idx[:M].cpu().numpy(), want_idx)
+    # two sampled rows per sequence: its first and last masked row
+    rows = np.unique(np.concatenate([want_off[:-1], want_off[1:] - 1]).astype(np.int64))
+    ref = oracle.masked_logits(wl.H, want_idx, wl.W, rows=rows)
+    assert_close(out[torch.from_numpy(rows).to(DEV)], ref, "ragged sampled rows")
+    other = m.mosaic_masked_logits(H, idx, W, M=M, chunk_rows=4096)
+    torch.cuda.synchronize()
+    assert torch.equal(other, out)
+
+
+def test_one_hot_full_shape_bit_exact(m):
+    # W[v, k] = [k == v mod d]: every logit is an exact copy of a gathered H element
+    wl = inputs.make_workload("long_logits")
+    d, V = wl.d, wl.V
+    W1 = inputs.one_hot_rows(V, d).to(DEV)
+    tok = wl.tokens.to(DEV)
+    idx, cnt = m.mosaic_mask_compact(tok, wl.mask_id)
+    M = int(cnt.item())
+    H = wl.H.to(DEV)
+    out = m.mosaic_masked_logits(H, idx, W1, M=M, chunk_rows=wl.chunk_rows)
+    cols = torch.arange(V, device=DEV) % d
+    for r0 in range(0, M, 2048):
+        r1 = min(M, r0 + 2048)
+        want = H[idx[r0:r1].long()][:, cols]
+        assert torch.equal(out[r0:r1], want), r0
+
+
+def test_integer_inputs_full_shape_bit_exact(m):
+    # integer-valued H, W in [-2, 2]: fp32 accumulation is exact, so bf16 outputs are the
+    # unique RNE of the exact oracle value
+    wl = inputs.make_workload("llada_step", with_weights=False)
+    L, d, V = wl.L, wl.d, wl.V
+    H = inputs.integer_valued(31, (L, d))
+    W = inputs.integer_valued(32, (V, d))
+    want = oracle.mask_compact(wl.tokens, wl.mask_id)
+    idx = torch.from_numpy(want).to(DEV)
+    out = m.mosaic_masked_logits(H.to(DEV), idx, W.to(DEV))
+    torch.cuda.synchronize()
+    rows = sample_rows(want.size, 0, 6, seed=5)
+    ref = oracle.masked_logits(H, want, W, rows=rows)
+    assert torch.equal(out[torch.from_numpy(rows).to(DEV)].cpu(), bf16_rne(ref))

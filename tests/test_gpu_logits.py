@@ -1,0 +1,157 @@
+"""GPU gather-GEMM vs the CPU oracle at sizes the oracle finishes in seconds.
+
+Shapes span several 256 x 256 tiles with ragged tails in M and V, odd and even
+K-tile counts, vocabulary sizes that are not multiples of 4 (scalar stores), the
+d % 64 != 0 kernel, all three dtype pairs, and row chunking.  Exact pins (integer
+inputs, one-hot weights) are compared bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mask_only_logits_amd import inputs
+from tests.helpers import assert_close, bf16_rne
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TD = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@pytest.fixture(scope="module")
+def m():
+    from mask_only_logits_amd import mosaic
+    return mosaic
+
+
+def _gpu_idx(wl):
+    idx = oracle.mask_compact(wl.tokens, wl.mask_id)
+    return idx, torch.from_numpy(idx).to(DEV)
+
+
+CASES = [
+    # (in, out, L, d, V, M, chunk_rows)
+    ("bf16", "bf16", 700, 512, 1000, 600, 0),
+    ("bf16", "bf16", 700, 512, 1000, 600, 256),
+    ("bf16", "bf16", 700, 512, 1000, 600, 77),
+    ("bf16", "bf16", 2000, 4096, 1500, 300, 0),
+    ("bf16", "bf16", 900, 3584, 700, 513, 200),
+    ("bf16", "bf16", 400, 64, 1001, 257, 0),        # one K tile; V % 4 != 0
+    ("bf16", "bf16", 400, 128, 257, 256, 0),        # two K tiles
+    ("bf16", "bf16", 400, 192, 255, 255, 0),        # three K tiles (odd)
+    ("bf16", "bf16", 300, 64, 3, 1, 0),             # a single row, tiny vocabulary
+    ("bf16", "bf16", 300, 320, 513, 2, 0),
+    ("bf16", "bf16", 300, 72, 300, 100, 0),         # d % 64 != 0 kernel
+    ("bf16", "bf16", 300, 8, 65, 33, 10),
+    ("bf16", "f32", 700, 512, 1000, 600, 0),
+    ("bf16", "f32", 300, 136, 129, 70, 0),
+    ("bf16", "f32", 300, 256, 130, 70, 0),
+    ("f32", "f32", 256, 256, 1024, 128, 0),
+    ("f32", "f32", 300, 100, 131, 77, 30),
+    ("f32", "f32", 70, 4, 1, 1, 0),
+]
+
+
+@pytest.mark.parametrize("dt_in,dt_out,L,d,V,M,C", CASES)
+def test_parity_random(m, dt_in, dt_out, L, d, V, M, C):
+    wl = inputs.make_random(L * 31 + d * 7 + V + M, L=L, d=d, V=V, M=M, dtype=dt_in, std_w=0.02)
+    idx, idx_d = _gpu_idx(wl)
+    out = m.mosaic_masked_logits(wl.H.to(DEV), idx_d, wl.W.to(DEV), chunk_rows=C, out_dtype=TD[dt_out])
+    torch.cuda.synchronize()
+    assert out.shape == (M, V) and out.dtype == TD[dt_out]
+    assert_close(out, oracle.masked_logits(wl.H, idx, wl.W), f"{dt_in}->{dt_out} {L},{d},{V},{M},{C}")
+
+
+@pytest.mark.parametrize("d,V,M", [(4096, 1000, 300), (512, 1001, 600), (72, 100, 50)])
+def test_exact_integers_bit_exact(m, d, V, M):
+    L = M + 50
+    H = inputs.integer_valued(d + 1, (L, d))
+    W = inputs.integer_valued(d + 2, (V, d))
+    idx = np.sort(np.random.default_rng(d).choice(L, M, replace=False)).astype(np.int32)
+    out = m.mosaic_masked_logits(H.to(DEV), torch.from_numpy(idx).to(DEV), W.to(DEV))
+    out32 = m.mosaic_masked_logits(H.to(DEV), torch.from_numpy(idx).to(DEV), W.to(DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.masked_logits(H, idx, W)           # exact integers (|x| <= 4d < 2^24)
+    assert np.array_equal(out32.cpu().numpy().astype(np.float64), ref)
+    assert torch.equal(out.cpu(), bf16_rne(ref))
+
+
+@pytest.mark.parametrize("d,V", [(256, 1000), (4096, 700), (64, 5)])
+def test_one_hot_weights_bit_exact(m, d, V):
+    wl = inputs.make_random(5 + d, L=500, d=d, V=V, M=333, dtype="bf16")
+    idx, idx_d = _gpu_idx(wl)
+    W = inputs.one_hot_rows(V, d)
+    out = m.mosaic_masked_logits(wl.H.to(DEV), idx_d, W.to(DEV))
+    torch.cuda.synchronize()
+    want = wl.H[torch.from_numpy(idx).long()][:, torch.arange(V) % d]
+    assert torch.equal(out.cpu(), want)
+
+
+def test_unsorted_and_repeated_rows(m):
+    wl = inputs.make_random(77, L=300, d=256, V=600, M=10, dtype="bf16")
+    idx = np.array([299, 0, 5, 5, 5, 17, 299, 3] * 40, np.int32)
+    out = m.mosaic_masked_logits(wl.H.to(DEV), torch.from_numpy(idx).to(DEV), wl.W.to(DEV))
+    torch.cuda.synchronize()
+    assert_close(out, oracle.masked_logits(wl.H, idx, wl.W), "unsorted")
+    o = out.cpu()
+    assert torch.equal(o[2], o[3]) and torch.equal(o[0], o[6])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_chunked_equals_unchunked_bit_exact(m, dt):
+    wl = inputs.make_random(99, L=1500, d=256, V=900, M=1100, dtype=dt)
+    _, idx_d = _gpu_idx(wl)
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    ref = m.mosaic_masked_logits(H, idx_d, W)
+    for C in (1, 63, 64, 255, 256, 257, 1000, 1099, 1100, 5000, -1):
+        got = m.mosaic_masked_logits(H, idx_d, W, chunk_rows=C)
+        assert torch.equal(got, ref), C
+    # streaming use: one call per chunk into a reused buffer
+    C = 300
+    buf = torch.empty((C, wl.V), dtype=ref.dtype, device=DEV)
+    for k in range(m.mosaic_num_chunks(1100, C)):
+        r0, r1 = k * C, min(1100, (k + 1) * C)
+        m.mosaic_masked_logits(H, idx_d[r0:r1], W, out=buf[: r1 - r0])
+        assert torch.equal(buf[: r1 - r0], ref[r0:r1]), k
+
+
+def test_permutation_and_scaling_invariants(m):
+    wl = inputs.make_random(7, L=800, d=512, V=700, M=600, dtype="bf16")
+    idx, idx_d = _gpu_idx(wl)
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    ref = m.mosaic_masked_logits(H, idx_d, W)
+    perm = torch.randperm(600, generator=torch.Generator().manual_seed(0))
+    got = m.mosaic_masked_logits(H, idx_d[perm.to(DEV)].contiguous(), W)
+    assert torch.equal(got, ref[perm.to(DEV)])
+    got2 = m.mosaic_masked_logits(H, idx_d, (W.float() * 2).to(torch.bfloat16))
+    assert torch.equal(got2, (ref.float() * 2).to(torch.bfloat16))
+
+
+def test_deterministic(m):
+    wl = inputs.make_random(8, L=1000, d=1024, V=1300, M=700, dtype="bf16")
+    _, idx_d = _gpu_idx(wl)
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    a = m.mosaic_masked_logits(H, idx_d, W)
+    b = m.mosaic_masked_logits(H, idx_d, W)
+    assert torch.equal(a, b)
+
+
+def test_zero_rows_leave_out_untouched(m):
+    wl = inputs.make_random(9, L=100, d=64, V=50, M=10, dtype="bf16")
+    _, idx_d = _gpu_idx(wl)
+    poison = torch.full((10, 50), 7.0, dtype=torch.bfloat16, device=DEV)
+    m.mosaic_masked_logits(wl.H.to(DEV), idx_d, wl.W.to(DEV), M=0, out=poison)
+    torch.cuda.synchronize()
+    assert bool((poison == 7.0).all())
+
+
+def test_rejected_call_leaves_out_untouched(m):
+    wl = inputs.make_random(10, L=100, d=64, V=50, M=10, dtype="bf16")
+    _, idx_d = _gpu_idx(wl)
+    poison = torch.full((10, 50), 7.0, dtype=torch.bfloat16, device=DEV)
+    H = wl.H.to(DEV)
+    with pytest.raises(m.MosaicError):
+        m.mosaic_masked_logits(H[:, :60].contiguous(), idx_d, wl.W.to(DEV)[:, :60].contiguous().view(-1)[: 50 * 60]
+                               .view(50, 60), out=poison)   # d = 60 is not a multiple of 8
+    torch.cuda.synchronize()
+    assert bool((poison == 7.0).all())
