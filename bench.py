@@ -78,6 +78,83 @@ def cpu_baseline(wl, idx_np, target_s: float):
                       f"(fp64, ascending k), {dt:.1f} s"}
 
 
+def _read_csv(path):
+    import csv
+    with open(path, newline="", encoding="utf-8") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _find(root, suffix):
+    out = []
+    for dirpath, _, files in os.walk(root):
+        out += [os.path.join(dirpath, f) for f in files if f.endswith(suffix)]
+    return sorted(out)
+
+
+def summarize_profile(root: str, workload: str, copy_mib: int):
+    """Write profiles/ summaries from rocprofv3 output under `root`: kernel_stats
+    (--kernel-trace --stats) and counter_collection (--pmc) CSV files.  `root/commands.txt`,
+    if present, holds the rocprofv3 command lines that produced them; it is copied in."""
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    stats = _find(root, "kernel_stats.csv")
+    counters = _find(root, "counter_collection.csv")
+    lines = [f"# rocprofv3 summary: gather-GEMM on workload {workload}", ""]
+    cmd_file = os.path.join(root, "commands.txt")
+    if os.path.exists(cmd_file):
+        lines += ["Commands (run from the repository root):", "```"]
+        lines += [ln.rstrip() for ln in open(cmd_file, encoding="utf-8") if ln.strip()]
+        lines += ["```", ""]
+    for f in stats:
+        rows = _read_csv(f)
+        lines.append(f"## {os.path.relpath(f, root)}")
+        lines.append("| kernel | calls | total ms | avg us | min us | max us | % |")
+        lines.append("|---|---|---|---|---|---|---|")
+        for r in rows:
+            lines.append("| {} | {} | {:.3f} | {:.1f} | {:.1f} | {:.1f} | {:.2f} |".format(
+                r["Name"][:90], r["Calls"], float(r["TotalDurationNs"]) / 1e6, float(r["AverageNs"]) / 1e3,
+                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+        lines.append("")
+    per_kernel = {}
+    for f in counters:
+        for r in _read_csv(f):
+            name = r.get("Kernel_Name", "")
+            key = ("gather_gemm" if "gather_gemm_bf16_kernel" in name else
+                   "copy" if "elementwise" in name or "mul" in name.lower() else None)
+            if key is None:
+                continue
+            c = r["Counter_Name"]
+            per_kernel.setdefault(key, {}).setdefault(c, []).append(float(r["Counter_Value"]))
+    if per_kernel:
+        lines.append("## counters (mean per dispatch)")
+        lines.append("| kernel | counter | dispatches | mean | ")
+        lines.append("|---|---|---|---|")
+        for k, cs in sorted(per_kernel.items()):
+            for c, v in sorted(cs.items()):
+                lines.append(f"| {k} | {c} | {len(v)} | {sum(v) / len(v):.6g} |")
+        lines.append("")
+    traffic = None
+    g, cp = per_kernel.get("gather_gemm", {}), per_kernel.get("copy", {})
+    if g.get("FETCH_SIZE") and g.get("WRITE_SIZE") and cp.get("FETCH_SIZE") and cp.get("WRITE_SIZE"):
+        known = copy_mib * (1 << 20)
+        f_scale = known / (sum(cp["FETCH_SIZE"]) / len(cp["FETCH_SIZE"]) * 1024)
+        w_scale = known / (sum(cp["WRITE_SIZE"]) / len(cp["WRITE_SIZE"]) * 1024)
+        fetch = sum(g["FETCH_SIZE"]) / len(g["FETCH_SIZE"]) * 1024 * f_scale
+        write = sum(g["WRITE_SIZE"]) / len(g["WRITE_SIZE"]) * 1024 * w_scale
+        traffic = {"kernel_source_hash": kernel_source_hash(), "workload": workload,
+                   "bytes_per_launch": int(fetch + write), "fetch_bytes_per_launch": int(fetch),
+                   "write_bytes_per_launch": int(write), "fetch_scale": f_scale, "write_scale": w_scale,
+                   "copy_probe_bytes": known}
+        with open(os.path.join(prof, f"traffic_gather_gemm_{workload}.json"), "w", encoding="utf-8") as fh:
+            json.dump(traffic, fh, indent=1)
+        lines.append(f"traffic per GEMM launch (scaled by the copy probe): fetch {fetch / 1e9:.3f} GB, "
+                     f"write {write / 1e9:.3f} GB (scales {f_scale:.4f}, {w_scale:.4f})")
+    out = os.path.join(prof, f"gather_gemm_{workload}_rocprof.md")
+    with open(out, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines) + "\n")
+    log(f"[bench] wrote {out}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -86,7 +163,16 @@ def main():
     ap.add_argument("--workload", default="long_logits")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-copy-mib", type=int, default=0,
+                    help="after the timed steps, run a plain elementwise copy of this many MiB three times "
+                         "(a kernel of known traffic that calibrates rocprofv3's FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="summarize rocprofv3 CSV output found under DIR into profiles/ and exit")
     args = ap.parse_args()
+
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.workload, args.profile_copy_mib or 1024)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path is a single-GPU kernel library); got --gpus {args.gpus}",
@@ -193,6 +279,16 @@ def main():
         "detail": {"gemm_ms_per_step": round(gemm_avg, 4), "gemm_ms_min": round(min(gemm_ms), 4),
                    "compaction_readback_us": round(float(np.mean(compact_ms)) * 1e3, 2)},
     }
+    if args.profile_copy_mib:
+        n = args.profile_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)      # reads and writes exactly n * 4 bytes
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] copy probe: 3 x {args.profile_copy_mib} MiB read + write")
+
     if not args.no_cpu_baseline:
         idx_np = idx[:M].cpu().numpy()
         log("[bench] timing the CPU oracle on a row sample ...")

@@ -18,7 +18,14 @@ enum LogitsVariant : int {
     kVariantF32 = 0,          // fp32 inputs: LDS-tiled FMA kernel
     kVariantBf16Tile256 = 1,  // bf16 inputs, d % 64 == 0: 256 x 256 MFMA tile, 2-stage LDS pipeline
     kVariantBf16Simple = 2,   // bf16 inputs, any d % 8 == 0: LDS-tiled FMA kernel
+    kVariantBf16K32S3 = 3,    // bf16, d % 32 == 0: 256 x 256 tile, K 32 deep, 3 LDS stages
+    kVariantBf16K32S4 = 4,    // ... 4 LDS stages
+    kVariantBf16K32S5 = 5,    // ... 5 LDS stages (160 KiB)
+    kNumVariants = 6,
 };
+
+// Default number of row tiles that share the W slabs of one XCD (tile order).
+constexpr int kDefaultGroupM = 4;
 
 // Whether a chunk of `rows` rows over V vocabulary rows fits the variant's launch grid.
 bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V);
@@ -26,6 +33,6 @@ bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V);
 // One chunk: out[i, v] for i < rows, v < V, out row stride ldo elements.
 hipError_t launch_gather_gemm(int variant, const void *H, const int32_t *idx, int64_t rows,
                               const void *W, int64_t V, int64_t d, void *out, int64_t ldo,
-                              bool out_bf16, hipStream_t stream);
+                              bool out_bf16, int group_m, hipStream_t stream);
 
 }  // namespace mosaic

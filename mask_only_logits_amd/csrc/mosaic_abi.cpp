@@ -11,6 +11,8 @@
 // touches neither the device nor `out`.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "../../include/mosaic.h"
 #include "launch.h"
@@ -36,18 +38,56 @@ int64_t checked_bytes(int64_t rows, int64_t V, int64_t esize)
     return n * esize;
 }
 
+// Debug/tuning override read on every call: MOSAIC_TUNE="variant=<n>,group_m=<g>".
+// A forced variant that cannot run the call's shape is ignored.
+struct Tune {
+    int variant = -1;
+    int group_m = 0;
+};
+
+Tune read_tune()
+{
+    Tune t;
+    const char *e = getenv("MOSAIC_TUNE");
+    if (!e)
+        return t;
+    const char *p;
+    if ((p = strstr(e, "variant=")))
+        t.variant = atoi(p + 8);
+    if ((p = strstr(e, "group_m=")))
+        t.group_m = atoi(p + 8);
+    return t;
+}
+
+bool variant_can_run(int v, int64_t d, mosaic_dtype_t in, mosaic_dtype_t out)
+{
+    const bool bf16_in = in == MOSAIC_BF16 && (out == MOSAIC_BF16 || out == MOSAIC_F32);
+    // The tiled kernels address a 256-row W slab with 32-bit byte offsets.
+    const bool small_d = d <= (1 << 22);
+    switch (v) {
+    case mosaic::kVariantF32: return in == MOSAIC_F32 && out == MOSAIC_F32 && d % 4 == 0;
+    case mosaic::kVariantBf16Simple: return bf16_in && d % 8 == 0;
+    case mosaic::kVariantBf16Tile256: return bf16_in && d % 64 == 0 && small_d;
+    case mosaic::kVariantBf16K32S3:
+    case mosaic::kVariantBf16K32S4:
+    case mosaic::kVariantBf16K32S5: return bf16_in && d % 32 == 0 && small_d;
+    default: return false;
+    }
+}
+
 int pick_variant(int64_t M, int64_t V, int64_t d, mosaic_dtype_t in, mosaic_dtype_t out)
 {
     (void)M;
     (void)V;
-    if (in == MOSAIC_F32 && out == MOSAIC_F32)
-        return d % 4 == 0 ? mosaic::kVariantF32 : -1;
-    if (in == MOSAIC_BF16 && (out == MOSAIC_BF16 || out == MOSAIC_F32)) {
-        if (d % 8 != 0)
-            return -1;
-        // The tiled kernel addresses a 256-row W slab with 32-bit byte offsets.
-        return (d % 64 == 0 && d <= (1 << 22)) ? mosaic::kVariantBf16Tile256 : mosaic::kVariantBf16Simple;
-    }
+    const Tune t = read_tune();
+    if (t.variant >= 0 && variant_can_run(t.variant, d, in, out))
+        return t.variant;
+    if (variant_can_run(mosaic::kVariantF32, d, in, out))
+        return mosaic::kVariantF32;
+    if (variant_can_run(mosaic::kVariantBf16Tile256, d, in, out))
+        return mosaic::kVariantBf16Tile256;
+    if (variant_can_run(mosaic::kVariantBf16Simple, d, in, out))
+        return mosaic::kVariantBf16Simple;
     return -1;
 }
 
@@ -159,12 +199,13 @@ mosaic_status_t mosaic_masked_logits(const void *H, int64_t L, int64_t d, const 
     if (C > kMaxPos || !mosaic::gather_gemm_grid_fits(variant, C, V))
         return MOSAIC_ERR_UNSUPPORTED;
     const bool out_bf16 = out_dtype == MOSAIC_BF16;
+    const int group_m = read_tune().group_m;
     for (int64_t k = 0; k < K; ++k) {
         const int64_t r0 = k * C;
         const int64_t r1 = (r0 + C < M) ? r0 + C : M;
         void *chunk_out = (char *)out + r0 * V * out_es;
         const hipError_t e = mosaic::launch_gather_gemm(variant, H, idx + r0, r1 - r0, W, V, d, chunk_out, V,
-                                                        out_bf16, (hipStream_t)stream);
+                                                        out_bf16, group_m, (hipStream_t)stream);
         if (e != hipSuccess)
             return MOSAIC_ERR_DEVICE;
     }
