@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <utility>
 
 #include "launch.h"
@@ -337,6 +338,169 @@ gather_gemm_bf16_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict_
     }
 }
 
+// Low-M gather-GEMM (M <= 32 * AM): the work is streaming W once from HBM.
+//
+// Every wave is an independent stream.  Wave w of the grid owns an equal, contiguous
+// range of vocabulary rows, so every wave streams the same number of W bytes.  It walks
+// its range in blocks of 32 rows (one MFMA A block), each block a full K loop, through
+// a private ring of NSTAGE LDS stages filled by its own global_load_lds DMA: the wave
+// waits on its own vmcnt and needs no workgroup barrier, and its ring keeps running
+// across blocks (the next block's first K tiles are in flight while the current block
+// finishes).  The masked rows (at most 32 * AM) are the MFMA B operand; each wave stages
+// its own copy per K tile from L2 (they are tiny).  Same MFMA, operand roles and k order
+// as the tiled kernel, so the results are bit-identical to it.
+template <int AM, int NSTAGE, bool OUT_BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
+gather_gemm_lowm_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict__ idx, int32_t rows,
+                        const __bf16 *__restrict__ W, int32_t V, int32_t d, void *__restrict__ out,
+                        int64_t ldo)
+{
+    constexpr int BK = 64, ROW_BYTES = 128, CHUNKS = 8, RPI = 8;
+    constexpr int W_TILE = 32 * ROW_BYTES;        // 4 KiB: the wave's 32 rows
+    constexpr int H_TILE = 32 * AM * ROW_BYTES;   // 4 or 8 KiB
+    constexpr int STAGE = W_TILE + H_TILE;
+    constexpr int WAVE_LDS = NSTAGE * STAGE;
+    constexpr int LW = W_TILE / 1024, LH = H_TILE / 1024;   // DMA instructions per tile
+    constexpr int T = LW + LH;
+    static_assert(4 * WAVE_LDS <= 160 * 1024, "LDS");
+    static_assert((NSTAGE - 1) * T < 64, "vmcnt");
+
+    __shared__ __attribute__((aligned(1024))) char smem_all[4 * WAVE_LDS];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    char *smem = smem_all + wave * WAVE_LDS;
+    const int64_t nw = (int64_t)gridDim.x * 4, gw = (int64_t)blockIdx.x * 4 + wave;
+    const int v_lo = (int)((gw * V) / nw);
+    const int v_hi = (int)(((gw + 1) * V) / nw);
+    const int nblocks = (v_hi - v_lo + 31) / 32;
+    const int nk = d / BK;
+    const int ntiles = nblocks * nk;              // flattened (block, k tile) stream
+
+    // DMA lanes: instruction j fills tile rows j*8 + lane/8, physical chunk lane%8.
+    int wch[LW];
+#pragma unroll
+    for (int j = 0; j < LW; ++j)
+        wch[j] = ((lane % CHUNKS) ^ swz<BK>(j * RPI + lane / CHUNKS)) * 16;
+    const char *hsrc[LH];
+#pragma unroll
+    for (int j = 0; j < LH; ++j) {
+        const int r = j * RPI + lane / CHUNKS;
+        hsrc[j] = (const char *)(H + (int64_t)idx[min(r, rows - 1)] * d) + ((lane % CHUNKS) ^ swz<BK>(r)) * 16;
+    }
+
+    auto issue = [&](int so, int g) {
+        const int blk = g / nk, kt = g - blk * nk;
+        const int kb = kt * ROW_BYTES;
+#pragma unroll
+        for (int j = 0; j < LW; ++j) {
+            const int v = min(v_lo + blk * 32 + j * RPI + lane / CHUNKS, v_hi - 1);
+            __builtin_amdgcn_global_load_lds((const void *)((const char *)(W + (int64_t)v * d) + kb + wch[j]),
+                                             (lds_void_t *)(smem + so + j * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < LH; ++j)
+            __builtin_amdgcn_global_load_lds((const void *)(hsrc[j] + kb),
+                                             (lds_void_t *)(smem + so + W_TILE + j * 1024), 16, 0, 0);
+    };
+
+    // At most n tiles of this wave's DMA still in flight (epilogue stores also count in
+    // vmcnt; they are younger than the loads waited for, so the wait is only stricter).
+    auto wait_tiles = [&](int n) {
+        if (NSTAGE >= 8 && n >= 7) wait_vmcnt<(NSTAGE >= 8 ? 7 : 0) * T>();
+        else if (NSTAGE >= 7 && n >= 6) wait_vmcnt<(NSTAGE >= 7 ? 6 : 0) * T>();
+        else if (NSTAGE >= 6 && n >= 5) wait_vmcnt<(NSTAGE >= 6 ? 5 : 0) * T>();
+        else if (NSTAGE >= 5 && n >= 4) wait_vmcnt<(NSTAGE >= 5 ? 4 : 0) * T>();
+        else if (NSTAGE >= 4 && n >= 3) wait_vmcnt<(NSTAGE >= 4 ? 3 : 0) * T>();
+        else if (NSTAGE >= 3 && n >= 2) wait_vmcnt<(NSTAGE >= 3 ? 2 : 0) * T>();
+        else if (n >= 1) wait_vmcnt<T>();
+        else wait_vmcnt<0>();
+    };
+
+    const int fr = lane & 31, hi = lane >> 5;
+    const int lane_chunk = (hi ^ swz<BK>(fr)) * 16;
+    const int a_addr = fr * ROW_BYTES + lane_chunk;
+    const int b_addr = W_TILE + fr * ROW_BYTES + lane_chunk;
+
+    f32x16_t acc[AM];
+#pragma unroll
+    for (int bm = 0; bm < AM; ++bm)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            acc[bm][e] = 0.0f;
+
+    const int npre = min(NSTAGE, ntiles);
+    for (int g = 0; g < npre; ++g)
+        issue(g * STAGE, g);
+
+    int rd = 0;
+    for (int g = 0; g < ntiles; ++g) {
+        wait_tiles(min(NSTAGE - 1, ntiles - 1 - g));   // tile g is in this wave's LDS
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
+            const bf16x8_t af = *(const bf16x8_t *)(smem + ((a_addr + rd) ^ (32 * s)));
+            bf16x8_t bf[AM];
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm)
+                bf[bm] = *(const bf16x8_t *)(smem + ((b_addr + rd + bm * 32 * ROW_BYTES) ^ (32 * s)));
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm)
+                acc[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[bm], acc[bm], 0, 0, 0);
+        }
+        if (g + NSTAGE < ntiles) {
+            wait_vmcnt<63>();   // lgkmcnt(0): this wave's reads of the stage are complete
+            issue(rd, g + NSTAGE);
+        }
+        rd = (rd + STAGE == WAVE_LDS) ? 0 : rd + STAGE;
+
+        const int blk = g / nk;
+        if (g - blk * nk == nk - 1) {
+            // block done: store its outputs and restart the accumulation
+            const int vb = v_lo + blk * 32;
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm) {
+                const int row = bm * 32 + fr;
+                if (row < rows) {
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int v = vb + gq * 8 + hi * 4;
+                        const float x0 = acc[bm][gq * 4 + 0], x1 = acc[bm][gq * 4 + 1];
+                        const float x2 = acc[bm][gq * 4 + 2], x3 = acc[bm][gq * 4 + 3];
+                        const bool full = v + 3 < v_hi && (ldo & 3) == 0;
+                        if constexpr (OUT_BF16) {
+                            __bf16 *o = (__bf16 *)out + (int64_t)row * ldo + v;
+                            if (full) {
+                                uint2 p;
+                                p.x = pack_bf16x2(x0, x1);
+                                p.y = pack_bf16x2(x2, x3);
+                                *(uint2 *)o = p;
+                            } else {
+                                if (v + 0 < v_hi) o[0] = static_cast<__bf16>(x0);
+                                if (v + 1 < v_hi) o[1] = static_cast<__bf16>(x1);
+                                if (v + 2 < v_hi) o[2] = static_cast<__bf16>(x2);
+                                if (v + 3 < v_hi) o[3] = static_cast<__bf16>(x3);
+                            }
+                        } else {
+                            float *o = (float *)out + (int64_t)row * ldo + v;
+                            if (full) {
+                                *(f32x4_t *)o = f32x4_t{x0, x1, x2, x3};
+                            } else {
+                                if (v + 0 < v_hi) o[0] = x0;
+                                if (v + 1 < v_hi) o[1] = x1;
+                                if (v + 2 < v_hi) o[2] = x2;
+                                if (v + 3 < v_hi) o[3] = x3;
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[bm][e] = 0.0f;
+            }
+        }
+    }
+}
+
 // bf16 inputs with d % 64 != 0 (any d % 8 == 0): 64 x 64 outputs per workgroup,
 // K staged 16 deep through LDS as fp32, fp32 FMA in ascending k.
 template <bool OUT_BF16>
@@ -477,6 +641,25 @@ hipError_t launch_bf16(const void *H, const int32_t *idx, int64_t rows, const vo
     return hipGetLastError();
 }
 
+template <int AM>
+hipError_t launch_lowm(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V, int64_t d,
+                       void *out, int64_t ldo, bool out_bf16, hipStream_t stream)
+{
+    constexpr int NSTAGE = AM == 1 ? 5 : 3;   // 40 KiB of LDS per wave
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    // one workgroup (four streams) per CU, but never fewer than 32 rows per stream
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cus, (V + 127) / 128));
+    if (out_bf16)
+        hipLaunchKernelGGL((gather_gemm_lowm_kernel<AM, NSTAGE, true>), dim3(grid), dim3(256), 0, stream,
+                           (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d, out, ldo);
+    else
+        hipLaunchKernelGGL((gather_gemm_lowm_kernel<AM, NSTAGE, false>), dim3(grid), dim3(256), 0, stream,
+                           (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d, out, ldo);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V)
@@ -490,6 +673,8 @@ bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V)
     case kVariantBf16K32S4:
     case kVariantBf16K32S5:
         return ((rows + 255) / 256) * ((V + 255) / 256) <= 0x7fffffffLL;
+    case kVariantBf16LowM:
+        return rows <= 64;
     default:
         return false;
     }
@@ -526,6 +711,10 @@ hipError_t launch_gather_gemm(int variant, const void *H, const int32_t *idx, in
         return launch_bf16<256, 256, 32, 4>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
     case kVariantBf16K32S5:
         return launch_bf16<256, 256, 32, 5>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
+    case kVariantBf16LowM:
+        if (rows <= 32)
+            return launch_lowm<1>(H, idx, rows, W, V, d, out, ldo, out_bf16, stream);
+        return launch_lowm<2>(H, idx, rows, W, V, d, out, ldo, out_bf16, stream);
     default:
         return hipErrorInvalidValue;
     }

@@ -21,7 +21,8 @@ enum LogitsVariant : int {
     kVariantBf16K32S3 = 3,    // bf16, d % 32 == 0: 256 x 256 tile, K 32 deep, 3 LDS stages
     kVariantBf16K32S4 = 4,    // ... 4 LDS stages
     kVariantBf16K32S5 = 5,    // ... 5 LDS stages (160 KiB)
-    kNumVariants = 6,
+    kVariantBf16LowM = 6,     // bf16, d % 64 == 0, M <= 64: W-streaming persistent kernel
+    kNumVariants = 7,
 };
 
 // Default number of row tiles that share the W slabs of one XCD (tile order).

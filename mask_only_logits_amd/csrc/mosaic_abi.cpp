@@ -59,7 +59,7 @@ Tune read_tune()
     return t;
 }
 
-bool variant_can_run(int v, int64_t d, mosaic_dtype_t in, mosaic_dtype_t out)
+bool variant_can_run(int v, int64_t M, int64_t d, mosaic_dtype_t in, mosaic_dtype_t out)
 {
     const bool bf16_in = in == MOSAIC_BF16 && (out == MOSAIC_BF16 || out == MOSAIC_F32);
     // The tiled kernels address a 256-row W slab with 32-bit byte offsets.
@@ -71,22 +71,24 @@ bool variant_can_run(int v, int64_t d, mosaic_dtype_t in, mosaic_dtype_t out)
     case mosaic::kVariantBf16K32S3:
     case mosaic::kVariantBf16K32S4:
     case mosaic::kVariantBf16K32S5: return bf16_in && d % 32 == 0 && small_d;
+    case mosaic::kVariantBf16LowM: return bf16_in && d % 64 == 0 && small_d && M <= 64;
     default: return false;
     }
 }
 
 int pick_variant(int64_t M, int64_t V, int64_t d, mosaic_dtype_t in, mosaic_dtype_t out)
 {
-    (void)M;
     (void)V;
     const Tune t = read_tune();
-    if (t.variant >= 0 && variant_can_run(t.variant, d, in, out))
+    if (t.variant >= 0 && variant_can_run(t.variant, M, d, in, out))
         return t.variant;
-    if (variant_can_run(mosaic::kVariantF32, d, in, out))
+    if (variant_can_run(mosaic::kVariantF32, M, d, in, out))
         return mosaic::kVariantF32;
-    if (variant_can_run(mosaic::kVariantBf16Tile256, d, in, out))
+    if (variant_can_run(mosaic::kVariantBf16LowM, M, d, in, out))
+        return mosaic::kVariantBf16LowM;
+    if (variant_can_run(mosaic::kVariantBf16Tile256, M, d, in, out))
         return mosaic::kVariantBf16Tile256;
-    if (variant_can_run(mosaic::kVariantBf16Simple, d, in, out))
+    if (variant_can_run(mosaic::kVariantBf16Simple, M, d, in, out))
         return mosaic::kVariantBf16Simple;
     return -1;
 }

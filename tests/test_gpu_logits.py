@@ -62,6 +62,43 @@ def test_parity_random(m, dt_in, dt_out, L, d, V, M, C):
     assert_close(out, oracle.masked_logits(wl.H, idx, wl.W), f"{dt_in}->{dt_out} {L},{d},{V},{M},{C}")
 
 
+LOWM_CASES = [
+    # (out, L, d, V, M): the low-M streaming kernel (M <= 64, d % 64 == 0)
+    ("bf16", 500, 3584, 5000, 20), ("bf16", 300, 64, 3, 1), ("bf16", 300, 128, 129, 2),
+    ("bf16", 300, 192, 1001, 31), ("bf16", 300, 256, 777, 32), ("bf16", 300, 256, 4097, 33),
+    ("bf16", 300, 512, 300, 63), ("bf16", 300, 512, 2000, 64), ("f32", 300, 256, 1031, 17),
+    ("f32", 300, 320, 515, 50),
+]
+
+
+@pytest.mark.parametrize("dt_out,L,d,V,M", LOWM_CASES)
+def test_parity_lowm(m, dt_out, L, d, V, M):
+    assert m.mosaic_logits_variant(M, V, d, torch.bfloat16, TD[dt_out]) == 6
+    wl = inputs.make_random(L + d + V + M, L=L, d=d, V=V, M=M, dtype="bf16")
+    idx, idx_d = _gpu_idx(wl)
+    out = m.mosaic_masked_logits(wl.H.to(DEV), idx_d, wl.W.to(DEV), out_dtype=TD[dt_out])
+    torch.cuda.synchronize()
+    assert_close(out, oracle.masked_logits(wl.H, idx, wl.W), f"lowm {d},{V},{M}")
+
+
+@pytest.mark.parametrize("M,d,V,out", [(20, 3584, 5000, "bf16"), (64, 256, 1001, "f32"), (700, 512, 1000, "bf16"),
+                                       (1, 64, 300, "bf16")])
+def test_bf16_variants_bit_identical(m, monkeypatch, M, d, V, out):
+    # every bf16 MFMA variant accumulates each output in the same MFMA k order
+    wl = inputs.make_random(M + d + V, L=max(M, 300), d=d, V=V, M=M, dtype="bf16")
+    _, idx_d = _gpu_idx(wl)
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    ref = m.mosaic_masked_logits(H, idx_d, W, out_dtype=TD[out])
+    for v in (1, 3, 4, 5, 6):
+        if v == 6 and M > 64:
+            continue
+        monkeypatch.setenv("MOSAIC_TUNE", f"variant={v}")
+        got = m.mosaic_masked_logits(H, idx_d, W, out_dtype=TD[out])
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), v
+    monkeypatch.delenv("MOSAIC_TUNE")
+
+
 @pytest.mark.parametrize("d,V,M", [(4096, 1000, 300), (512, 1001, 600), (72, 100, 50)])
 def test_exact_integers_bit_exact(m, d, V, M):
     L = M + 50
