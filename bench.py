@@ -119,8 +119,8 @@ def summarize_profile(root: str, workload: str, copy_mib: int):
     for f in counters:
         for r in _read_csv(f):
             name = r.get("Kernel_Name", "")
-            key = ("gather_gemm" if "gather_gemm_bf16_kernel" in name else
-                   "copy" if "elementwise" in name or "mul" in name.lower() else None)
+            key = ("gather_gemm" if "gather_gemm_" in name and "simple" not in name else
+                   "copy" if "MulFunctor" in name or "AUnaryFunctor" in name else None)
             if key is None:
                 continue
             c = r["Counter_Name"]
@@ -252,8 +252,23 @@ def main():
         f"(min {min(gemm_ms):.3f}) = {achieved:.1f} TFLOP/s = {achieved / PEAK_BF16_TFLOPS:.1%} of bf16 peak; "
         f"{gemm_avg / launches:.3f} ms per launch; compaction+readback {np.mean(compact_ms) * 1e3:.1f} us")
 
-    alg_bytes = launches * V * d * 2 + M * d * 2 + M * V * out.element_size() + M * 4
+    esize_in = 2 if wl.dtype == "bf16" else 4
+    alg_bytes = launches * V * d * esize_in + M * d * esize_in + M * V * out.element_size() + M * 4
     traffic = measured_traffic(args.workload)
+    variant = mosaic.mosaic_logits_variant(M, V, d, H.dtype, out_dtype)
+    kernel = {0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel",
+              6: "gather_gemm_lowm_kernel"}.get(variant, "gather_gemm_bf16_kernel")
+    if variant == 6:
+        # streaming W is the bound: algorithmic bytes per launch over the launch time
+        achieved_gbs = alg_bytes / launches / (gemm_avg / launches / 1e3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+    roofline.update({"kernel": kernel, "launch_ms_avg": round(gemm_avg / launches, 4),
+                     "algorithmic_bytes_per_launch": int(alg_bytes / launches),
+                     "algorithmic_flop_per_launch": int(flop / launches)})
     result = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -270,12 +285,7 @@ def main():
         "config": {"workload": args.workload, "L": L, "d": d, "V": V, "M": M, "chunk_rows": C,
                    "launches_per_step": launches, "in_dtype": wl.dtype, "out_dtype": wl.out_dtype,
                    "accumulate": "fp32"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic,
-                     "kernel": "gather_gemm_bf16_kernel", "launch_ms_avg": round(gemm_avg / launches, 4),
-                     "algorithmic_bytes_per_launch": int(alg_bytes / launches),
-                     "hbm_frac_algorithmic": round(alg_bytes / (gemm_avg / 1e3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "roofline": roofline,
         "detail": {"gemm_ms_per_step": round(gemm_avg, 4), "gemm_ms_min": round(min(gemm_ms), 4),
                    "compaction_readback_us": round(float(np.mean(compact_ms)) * 1e3, 2)},
     }
