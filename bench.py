@@ -211,8 +211,9 @@ def main():
     C = wl.chunk_rows
     launches = mosaic.mosaic_num_chunks(M, C)
     flop = 2.0 * M * d * V
-    log(f"[bench] M={M} chunk_rows={C} launches={launches} variant="
-        f"{mosaic.mosaic_logits_variant(M, V, d, H.dtype, out_dtype)} out={out.numel() * out.element_size() / 1e9:.2f} GB")
+    rows_per_launch = M if launches == 1 else C
+    variant = mosaic.mosaic_logits_variant(rows_per_launch, V, d, H.dtype, out_dtype)
+    log(f"[bench] M={M} chunk_rows={C} launches={launches} variant={variant} out={out.numel() * out.element_size() / 1e9:.2f} GB")
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -255,9 +256,9 @@ def main():
     esize_in = 2 if wl.dtype == "bf16" else 4
     alg_bytes = launches * V * d * esize_in + M * d * esize_in + M * V * out.element_size() + M * 4
     traffic = measured_traffic(args.workload)
-    variant = mosaic.mosaic_logits_variant(M, V, d, H.dtype, out_dtype)
-    kernel = {0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel",
-              6: "gather_gemm_lowm_kernel"}.get(variant, "gather_gemm_bf16_kernel")
+    kernel = {0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel", 6: "gather_gemm_lowm_kernel",
+              9: "gather_gemm_bf16_persist_kernel", 10: "gather_gemm_bf16_persist_kernel",
+              11: "gather_gemm_bf16_persist_kernel"}.get(variant, "gather_gemm_bf16_kernel")
     if variant == 6:
         # streaming W is the bound: algorithmic bytes per launch over the launch time
         achieved_gbs = alg_bytes / launches / (gemm_avg / launches / 1e3) / 1e9

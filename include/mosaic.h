@@ -107,10 +107,11 @@ mosaic_status_t mosaic_mask_compact_batched(const int32_t *tokens, int64_t L,
  *   W      [V, d] row-major, in_dtype   LM-head weight (K-contiguous rows).
  *   out    [M, V] row-major, out_dtype  row i holds the logits of position idx[i].
  *   chunk_rows  max_num_logits: <= 0 or >= M runs one chunk; otherwise
- *               ceil(M / chunk_rows) chunks [k*C, min(M, (k+1)*C)).  The kernel
- *               variant is chosen once per call from M, so every chunk of a call
- *               uses the same one and the output is bit-identical for every
- *               chunk_rows value.
+ *               ceil(M / chunk_rows) chunks [k*C, min(M, (k+1)*C)).  Every chunk
+ *               runs the kernel variant chosen for C rows, except a last chunk of at
+ *               most 64 rows, which may take the low-M streaming kernel.  All variants
+ *               that one (d, dtype pair) can select add each output's products in the
+ *               same order, so the output is bit-identical for every chunk_rows value.
  * Dtype pairs (in -> out): F32->F32, BF16->BF16, BF16->F32.  Products are
  * accumulated in fp32 (bf16 MFMA with fp32 accumulators; fp32 FMA for F32 inputs);
  * bf16 outputs are rounded to nearest even.
@@ -137,8 +138,9 @@ int64_t mosaic_num_chunks(int64_t M, int64_t chunk_rows);
  * an unknown dtype, a NULL `bytes` or overflow of int64. */
 mosaic_status_t mosaic_logits_bytes(int64_t rows, int64_t V, mosaic_dtype_t dt, int64_t *bytes);
 
-/* Which kernel variant mosaic_masked_logits runs for M rows of this dtype pair
- * (a stable small integer, for tests and profiles), or -1 if unsupported. */
+/* Which kernel variant mosaic_masked_logits runs for one launch (one chunk) of M
+ * rows of this dtype pair (a stable small integer, for tests and profiles), or -1 if
+ * unsupported. */
 int mosaic_logits_variant(int64_t M, int64_t V, int64_t d, mosaic_dtype_t in_dtype,
                           mosaic_dtype_t out_dtype);
 

@@ -91,7 +91,7 @@ __device__ __forceinline__ int swz(int r)
         return (r >> 2) & 3;                      // 4 chunks per row; rows r, r+4, r+8, r+12
 }
 
-template <int BV, int BM, int BK, int NSTAGE, bool OUT_BF16>
+template <int BV, int BM, int BK, int NSTAGE, int NSPREAD, bool OUT_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
 gather_gemm_bf16_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict__ idx, int32_t rows,
                         const __bf16 *__restrict__ W, int32_t V, int32_t d, void *__restrict__ out,
@@ -193,6 +193,24 @@ gather_gemm_bf16_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict_
                                              0, 0);
     };
 
+    // Part p of NSPREAD of the DMA of K tile kt (W instructions first, then H).
+    auto issue_part = [&](int so, int kt, int p) {
+        constexpr int PER = (LW + LH) / NSPREAD;
+        const int kb = kt * ROW_BYTES;
+#pragma unroll
+        for (int i = 0; i < LW + LH; ++i) {
+            if (i / PER != p)
+                continue;
+            if (i < LW)
+                __builtin_amdgcn_global_load_lds((const void *)(wbase + kb + woff[i]),
+                                                 (lds_void_t *)(smem + so + (wave * LW + i) * 1024), 16, 0, 0);
+            else
+                __builtin_amdgcn_global_load_lds((const void *)(hsrc[i - LW] + kb),
+                                                 (lds_void_t *)(smem + so + W_TILE + (wave * LH + i - LW) * 1024),
+                                                 16, 0, 0);
+        }
+    };
+
     // Fragments of k sub-step s from the stage at byte offset `so`.
     auto load_frags = [&](int so, int s, bf16x8_t (&af)[AV], bf16x8_t (&bf)[AM]) {
         const int ab = (a_addr + so) ^ (32 * s), bb = (b_addr + so) ^ (32 * s);
@@ -258,31 +276,50 @@ gather_gemm_bf16_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict_
 
     int rd = 0;                               // byte offset of stage kt % NSTAGE
     int kt = 0;
-    // Steady state: every step refills a stage; branch-free body.
+    // Steady state: every step refills a stage.  sched_barrier(0) fences each k sub-step,
+    // so at most NFR (8) fragment reads are in flight: lgkmcnt is a 4-bit counter, and a
+    // longer run of reads makes the compiler wait for all of them.  The refill's DMA
+    // instructions are spread over NSPREAD sub-steps (the last one of this step and the
+    // first NSPREAD-1 of the next): a CU's texture path moves ~64 bytes per clock, so a
+    // whole 64 KiB refill issued inside one sub-step stalls the wave's MFMA issue.
+    static_assert(NSPREAD >= 1 && NSPREAD <= NSUB && (LW + LH) % NSPREAD == 0, "spread");
+    constexpr int PER = (LW + LH) / NSPREAD;
+    int pso = 0;   // stage of the refill still being issued (parts 1 .. NSPREAD-1)
+    bool pending = false;
     for (; kt + NSTAGE < nk; ++kt) {
 #pragma unroll
         for (int s = 0; s + 1 < NSUB; ++s) {
+            if (s + 1 < NSPREAD && pending)
+                issue_part(pso, kt - 1 + NSTAGE, s + 1);
             load_frags(rd, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
             mma(af[s & 1], bf[s & 1]);
-            interleave(0);
+            interleave(s + 1 < NSPREAD ? PER : 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
         wait_tiles(NSTAGE - 2);
         barrier_no_fence();
-        issue(rd, kt + NSTAGE);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_part(rd, kt + NSTAGE, 0);
+        pso = rd;
+        pending = NSPREAD > 1;
         const int nx = (rd + STAGE == NSTAGE * STAGE) ? 0 : rd + STAGE;
         load_frags(nx, 0, af[NSUB & 1], bf[NSUB & 1]);
         mma(af[(NSUB - 1) & 1], bf[(NSUB - 1) & 1]);
-        interleave(NDMA);
+        interleave(PER);
+        __builtin_amdgcn_sched_barrier(0);
         rd = nx;
         // NSUB is even, so af[0] / bf[0] again hold sub-step 0 of the next tile.
     }
-    // Drain: no more requests.
+    // Drain: no more requests (the parts of the last refill still pending go first).
     for (; kt < nk; ++kt) {
 #pragma unroll
         for (int s = 0; s + 1 < NSUB; ++s) {
+            if (s + 1 < NSPREAD && pending)
+                issue_part(pso, kt - 1 + NSTAGE, s + 1);
             load_frags(rd, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
             mma(af[s & 1], bf[s & 1]);
         }
+        pending = false;
         if (kt + 1 < nk) {
             wait_tiles(nk - 2 - kt);
             barrier_no_fence();
@@ -335,6 +372,328 @@ gather_gemm_bf16_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict_
                 }
             }
         }
+    }
+}
+
+// Persistent form of the tiled kernel: one workgroup per CU walks a list of 256 x 256
+// output tiles as one continuous stream of (tile, K tile) steps.
+//  * XCD x (hardware block b runs on XCD b % 8) owns a contiguous range of logical tiles
+//    in the grouped order; its G/8 workgroups take consecutive tiles of that range in
+//    lockstep (tile start_x + slot + i * G/8), so the workgroups resident on one XCD at a
+//    time share W slabs and H row blocks in its L2.
+//  * The DMA stream runs ahead across tile boundaries: the next tile's first K tiles
+//    are in flight while the current tile's last steps and epilogue run, and the next
+//    tile's H row indices are loaded a whole tile ahead.
+//  * Epilogue stores are 16 bytes per lane for bf16 output: permlane32_swap gives each
+//    lane eight consecutive vocabulary entries.
+// The k order of every output element is the tiled kernel's, so results are
+// bit-identical to it.
+template <int BK, int NSTAGE, int NSPREAD, bool OUT_BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
+gather_gemm_bf16_persist_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict__ idx, int32_t rows,
+                                const __bf16 *__restrict__ W, int32_t V, int32_t d, void *__restrict__ out,
+                                int64_t ldo, int32_t group_m)
+{
+    constexpr int BV = 256, BM = 256;
+    constexpr int ROW_BYTES = BK * 2;
+    constexpr int CHUNKS = BK / 8;
+    constexpr int RPI = 64 / CHUNKS;
+    constexpr int W_TILE = BV * ROW_BYTES;
+    constexpr int H_TILE = BM * ROW_BYTES;
+    constexpr int STAGE = W_TILE + H_TILE;
+    constexpr int WV = BV / 2, WM = BM / 2;
+    constexpr int AV = WV / 32, AM = WM / 32;
+    constexpr int LW = BV / RPI / 4, LH = BM / RPI / 4;
+    constexpr int NSUB = BK / 16;
+    constexpr int NDMA = LW + LH;
+    constexpr int NFR = AV + AM;
+    static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS");
+    static_assert(NSTAGE >= 2 && NSUB % 2 == 0, "pipeline");
+    static_assert(NSPREAD >= 1 && NSPREAD <= NSUB && NDMA % NSPREAD == 0, "spread");
+    constexpr int PER = NDMA / NSPREAD;
+
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+
+    const int nvt = (V + BV - 1) / BV;
+    const int nmt = (rows + BM - 1) / BM;
+    const int ntiles = nvt * nmt;
+    const int nk = d / BK;
+
+    // ---- this workgroup's tile list
+    const int G = gridDim.x;                    // a multiple of 8
+    const int per_xcd = G >> 3;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int q = ntiles >> 3, rem = ntiles & 7;
+    const int start = xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q;
+    const int count = q + (xcd < rem ? 1 : 0);
+    const int n_my = slot < count ? (count - slot + per_xcd - 1) / per_xcd : 0;
+    const int total = n_my * nk;                // steps of this workgroup
+    if (total == 0)
+        return;
+    auto tile_coords = [&](int i, int &m0, int &v0) {
+        const int t = start + slot + i * per_xcd;
+        const int per_group = group_m * nvt;
+        const int g = t / per_group;
+        const int first_m = g * group_m;
+        const int gsz = min(nmt - first_m, group_m);
+        const int local = t - g * per_group;
+        m0 = (first_m + local % gsz) * BM;
+        v0 = (local / gsz) * BV;
+    };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wv = wave & 1, wm = wave >> 1;
+
+    // ---- per-tile DMA sources, for the current and the next tile of the list
+    struct Src {
+        const char *wbase;
+        uint32_t woff[LW];
+        const char *hsrc[LH];
+    };
+    auto row_w = [&](int j) { return (wave * LW + j) * RPI + lane / CHUNKS; };
+    auto row_h = [&](int j) { return (wave * LH + j) * RPI + lane / CHUNKS; };
+    auto chunk_of = [&](int r) { return ((lane % CHUNKS) ^ swz<BK>(r)) * 16; };
+    int32_t hidx_nxt[LH];                       // H row ids of the next tile (loaded a tile ahead)
+    auto load_hidx = [&](int i) {
+        if (i >= n_my)
+            return;
+        int m0, v0;
+        tile_coords(i, m0, v0);
+#pragma unroll
+        for (int j = 0; j < LH; ++j)
+            hidx_nxt[j] = idx[min(m0 + row_h(j), rows - 1)];
+    };
+    auto make_src = [&](int i, Src &sr) {
+        int m0, v0;
+        tile_coords(min(i, n_my - 1), m0, v0);
+        sr.wbase = (const char *)(W + (int64_t)v0 * d);
+#pragma unroll
+        for (int j = 0; j < LW; ++j) {
+            const int vr = min(v0 + row_w(j), V - 1) - v0;
+            sr.woff[j] = (uint32_t)vr * (uint32_t)d * 2u + (uint32_t)chunk_of(row_w(j));
+        }
+#pragma unroll
+        for (int j = 0; j < LH; ++j)
+            sr.hsrc[j] = (const char *)(H + (int64_t)hidx_nxt[j] * d) + chunk_of(row_h(j));
+    };
+    Src cur;
+    load_hidx(0);
+    make_src(0, cur);
+    load_hidx(1);
+
+    // DMA of instructions [p*PER, (p+1)*PER) of K tile kt of the output tile whose
+    // sources are `sr`, into the stage at byte offset `so`
+    auto issue_part = [&](const Src &sr, int so, int kt, int p) {
+        const int kb = kt * ROW_BYTES;
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            if (i / PER != p)
+                continue;
+            if (i < LW)
+                __builtin_amdgcn_global_load_lds((const void *)(sr.wbase + kb + sr.woff[i]),
+                                                 (lds_void_t *)(smem + so + (wave * LW + i) * 1024), 16, 0, 0);
+            else
+                __builtin_amdgcn_global_load_lds((const void *)(sr.hsrc[i - LW] + kb),
+                                                 (lds_void_t *)(smem + so + W_TILE + (wave * LH + i - LW) * 1024),
+                                                 16, 0, 0);
+        }
+    };
+
+    f32x16_t acc[AV][AM];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int a = 0; a < AV; ++a)
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[a][bm][e] = 0.0f;
+    };
+    zero_acc();
+
+    const int fr = lane & 31, hi = lane >> 5;
+    const int lane_chunk = (hi ^ swz<BK>(fr)) * 16;
+    const int a_addr = (wv * WV + fr) * ROW_BYTES + lane_chunk;
+    const int b_addr = W_TILE + (wm * WM + fr) * ROW_BYTES + lane_chunk;
+
+    auto load_frags = [&](int so, int s, bf16x8_t (&af)[AV], bf16x8_t (&bf)[AM]) {
+        const int ab = (a_addr + so) ^ (32 * s), bb = (b_addr + so) ^ (32 * s);
+#pragma unroll
+        for (int a = 0; a < AV; ++a)
+            af[a] = *(const bf16x8_t *)(smem + ab + a * 32 * ROW_BYTES);
+#pragma unroll
+        for (int bm = 0; bm < AM; ++bm)
+            bf[bm] = *(const bf16x8_t *)(smem + bb + bm * 32 * ROW_BYTES);
+    };
+    auto mma = [&](const bf16x8_t (&af)[AV], const bf16x8_t (&bf)[AM]) {
+#pragma unroll
+        for (int a = 0; a < AV; ++a)
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm)
+                acc[a][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bf[bm], acc[a][bm], 0, 0, 0);
+    };
+    auto wait_tiles = [&](int n) {
+        if (NSTAGE >= 5 && n >= 4) wait_vmcnt<(NSTAGE >= 5 ? 4 : 0) * NDMA>();
+        else if (NSTAGE >= 4 && n >= 3) wait_vmcnt<(NSTAGE >= 4 ? 3 : 0) * NDMA>();
+        else if (NSTAGE >= 3 && n >= 2) wait_vmcnt<(NSTAGE >= 3 ? 2 : 0) * NDMA>();
+        else if (n >= 1) wait_vmcnt<NDMA>();
+        else wait_vmcnt<0>();
+    };
+    auto interleave = [&](int nvm) {
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            if (i < nvm) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NFR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+
+    // Epilogue of tile i: lane holds, for block (a, bm) and group gq, vocabulary entries
+    // v = v0 + wv*WV + 32a + 8gq + 4hi + (0..3) of masked row m0 + wm*WM + 32bm + fr.
+    // 16-byte stores need a 16-byte aligned row start
+    const bool vec_ok = ((uintptr_t)out & 15) == 0 && (ldo & (OUT_BF16 ? 7 : 3)) == 0;
+    auto epilogue = [&](int i) {
+        int m0, v0;
+        tile_coords(i, m0, v0);
+#pragma unroll
+        for (int bm = 0; bm < AM; ++bm) {
+            const int row = m0 + wm * WM + bm * 32 + fr;
+            const bool row_ok = row < rows;
+#pragma unroll
+            for (int a = 0; a < AV; ++a) {
+                const int vb = v0 + wv * WV + a * 32;
+                if constexpr (OUT_BF16) {
+                    uint32_t pk[4][2];
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        pk[gq][0] = pack_bf16x2(acc[a][bm][gq * 4 + 0], acc[a][bm][gq * 4 + 1]);
+                        pk[gq][1] = pack_bf16x2(acc[a][bm][gq * 4 + 2], acc[a][bm][gq * 4 + 3]);
+                    }
+                    // lanes 0-31 collect v 0..7 / 16..23, lanes 32-63 v 8..15 / 24..31
+#pragma unroll
+                    for (int pr = 0; pr < 2; ++pr) {
+                        const auto s0 = __builtin_amdgcn_permlane32_swap(pk[2 * pr][0], pk[2 * pr + 1][0], false, false);
+                        const auto s1 = __builtin_amdgcn_permlane32_swap(pk[2 * pr][1], pk[2 * pr + 1][1], false, false);
+                        const int v = vb + 16 * pr + 8 * hi;
+                        __bf16 *o = (__bf16 *)out + (int64_t)row * ldo + v;
+                        if (!row_ok)
+                            continue;   // (after the swaps: every lane takes part in them)
+                        if (vec_ok && v + 7 < V) {
+                            *(uint4 *)o = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+                        } else {
+                            const uint32_t w4[4] = {s0[0], s1[0], s0[1], s1[1]};
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                if (v + e < V)
+                                    o[e] = __builtin_bit_cast(__bf16, (uint16_t)(w4[e >> 1] >> (16 * (e & 1))));
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int v = vb + gq * 8 + hi * 4;
+                        float *o = (float *)out + (int64_t)row * ldo + v;
+                        const float x0 = acc[a][bm][gq * 4 + 0], x1 = acc[a][bm][gq * 4 + 1];
+                        const float x2 = acc[a][bm][gq * 4 + 2], x3 = acc[a][bm][gq * 4 + 3];
+                        if (!row_ok)
+                            continue;
+                        if (vec_ok && v + 3 < V) {
+                            *(f32x4_t *)o = f32x4_t{x0, x1, x2, x3};
+                        } else {
+                            if (v + 0 < V) o[0] = x0;
+                            if (v + 1 < V) o[1] = x1;
+                            if (v + 2 < V) o[2] = x2;
+                            if (v + 3 < V) o[3] = x3;
+                        }
+                    }
+                }
+                // this block is stored: restart its accumulation (keeps one block in VGPRs)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[a][bm][e] = 0.0f;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
+    // ---- per tile: the tiled kernel's pipeline.  The next tile's first NSTAGE K tiles
+    // are requested right after the last MFMAs of a tile have their operands, so they are
+    // in flight while the epilogue stores run.
+    bf16x8_t af[2][AV], bf[2][AM];
+    const int npre = min(NSTAGE, nk);
+    for (int s = 0; s < npre; ++s)
+#pragma unroll
+        for (int p = 0; p < NSPREAD; ++p)
+            issue_part(cur, s * STAGE, s, p);
+
+    for (int i = 0; i < n_my; ++i) {
+        wait_tiles(npre - 1);
+        barrier_no_fence();
+        load_frags(0, 0, af[0], bf[0]);
+        int rd = 0, pso = 0, pkt = 0;
+        bool pending = false;
+        int kt = 0;
+        for (; kt + NSTAGE < nk; ++kt) {
+#pragma unroll
+            for (int s = 0; s + 1 < NSUB; ++s) {
+                if (s + 1 < NSPREAD && pending)
+                    issue_part(cur, pso, pkt, s + 1);
+                load_frags(rd, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+                mma(af[s & 1], bf[s & 1]);
+                interleave(s + 1 < NSPREAD ? PER : 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            wait_tiles(NSTAGE - 2);
+            barrier_no_fence();
+            __builtin_amdgcn_sched_barrier(0);
+            issue_part(cur, rd, kt + NSTAGE, 0);
+            pso = rd;
+            pkt = kt + NSTAGE;
+            pending = NSPREAD > 1;
+            const int nx = (rd + STAGE == NSTAGE * STAGE) ? 0 : rd + STAGE;
+            load_frags(nx, 0, af[NSUB & 1], bf[NSUB & 1]);
+            mma(af[(NSUB - 1) & 1], bf[(NSUB - 1) & 1]);
+            interleave(PER);
+            __builtin_amdgcn_sched_barrier(0);
+            rd = nx;
+        }
+        for (; kt < nk; ++kt) {
+#pragma unroll
+            for (int s = 0; s + 1 < NSUB; ++s) {
+                if (s + 1 < NSPREAD && pending)
+                    issue_part(cur, pso, pkt, s + 1);
+                load_frags(rd, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+                mma(af[s & 1], bf[s & 1]);
+            }
+            pending = false;
+            if (kt + 1 < nk) {
+                wait_tiles(nk - 2 - kt);
+                barrier_no_fence();
+                rd = (rd + STAGE == NSTAGE * STAGE) ? 0 : rd + STAGE;
+                load_frags(rd, 0, af[NSUB & 1], bf[NSUB & 1]);
+            }
+            mma(af[(NSUB - 1) & 1], bf[(NSUB - 1) & 1]);
+        }
+        // every wave's last fragments are in registers: the stages are free
+        wait_vmcnt<63>();
+        barrier_no_fence();
+        if (i + 1 < n_my) {
+            make_src(i + 1, cur);
+            for (int s = 0; s < npre; ++s)
+#pragma unroll
+                for (int p = 0; p < NSPREAD; ++p)
+                    issue_part(cur, s * STAGE, s, p);
+        }
+        epilogue(i);   // also restarts the accumulators
+        load_hidx(i + 2);
     }
 }
 
@@ -624,20 +983,42 @@ __global__ __launch_bounds__(256) void gather_gemm_f32_kernel(const float *__res
     }
 }
 
-template <int BV, int BM, int BK, int NSTAGE>
+template <int BV, int BM, int BK, int NSTAGE, int NSPREAD = 1>
 hipError_t launch_bf16(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V, int64_t d,
                        void *out, int64_t ldo, bool out_bf16, int group_m, hipStream_t stream)
 {
     const int64_t nvt = (V + BV - 1) / BV, nmt = (rows + BM - 1) / BM;
     const dim3 grid((unsigned)(nvt * nmt));
     if (out_bf16)
-        hipLaunchKernelGGL((gather_gemm_bf16_kernel<BV, BM, BK, NSTAGE, true>), grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((gather_gemm_bf16_kernel<BV, BM, BK, NSTAGE, NSPREAD, true>), grid, dim3(256), 0, stream,
                            (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d, out,
                            ldo, group_m);
     else
-        hipLaunchKernelGGL((gather_gemm_bf16_kernel<BV, BM, BK, NSTAGE, false>), grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((gather_gemm_bf16_kernel<BV, BM, BK, NSTAGE, NSPREAD, false>), grid, dim3(256), 0, stream,
                            (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d, out,
                            ldo, group_m);
+    return hipGetLastError();
+}
+
+template <int BK, int NSTAGE, int NSPREAD>
+hipError_t launch_persist(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V, int64_t d,
+                          void *out, int64_t ldo, bool out_bf16, int group_m, hipStream_t stream)
+{
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t ntiles = ((V + 255) / 256) * ((rows + 255) / 256);
+    // one workgroup per CU (a multiple of 8: one set per XCD), no more than there are tiles
+    int64_t grid = std::max<int64_t>(8, (cus / 8) * 8);
+    grid = std::min<int64_t>(grid, ((ntiles + 7) / 8) * 8);
+    if (out_bf16)
+        hipLaunchKernelGGL((gather_gemm_bf16_persist_kernel<BK, NSTAGE, NSPREAD, true>), dim3((unsigned)grid), dim3(256),
+                           0, stream, (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d,
+                           out, ldo, group_m);
+    else
+        hipLaunchKernelGGL((gather_gemm_bf16_persist_kernel<BK, NSTAGE, NSPREAD, false>), dim3((unsigned)grid), dim3(256),
+                           0, stream, (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d,
+                           out, ldo, group_m);
     return hipGetLastError();
 }
 
@@ -672,6 +1053,11 @@ bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V)
     case kVariantBf16K32S3:
     case kVariantBf16K32S4:
     case kVariantBf16K32S5:
+    case kVariantBf16K64Spread2:
+    case kVariantBf16K64Spread4:
+    case kVariantBf16PersistK64:
+    case kVariantBf16PersistK64S4:
+    case kVariantBf16PersistK32:
         return ((rows + 255) / 256) * ((V + 255) / 256) <= 0x7fffffffLL;
     case kVariantBf16LowM:
         return rows <= 64;
@@ -706,11 +1092,21 @@ hipError_t launch_gather_gemm(int variant, const void *H, const int32_t *idx, in
     case kVariantBf16Tile256:
         return launch_bf16<256, 256, 64, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
     case kVariantBf16K32S3:
-        return launch_bf16<256, 256, 32, 3>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
+        return launch_bf16<256, 256, 32, 3, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
     case kVariantBf16K32S4:
-        return launch_bf16<256, 256, 32, 4>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
+        return launch_bf16<256, 256, 32, 4, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
     case kVariantBf16K32S5:
-        return launch_bf16<256, 256, 32, 5>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
+        return launch_bf16<256, 256, 32, 5, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
+    case kVariantBf16K64Spread2:
+        return launch_bf16<256, 256, 64, 2, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
+    case kVariantBf16K64Spread4:
+        return launch_bf16<256, 256, 64, 2, 4>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
+    case kVariantBf16PersistK64:
+        return launch_persist<64, 2, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
+    case kVariantBf16PersistK64S4:
+        return launch_persist<64, 2, 4>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
+    case kVariantBf16PersistK32:
+        return launch_persist<32, 4, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
     case kVariantBf16LowM:
         if (rows <= 32)
             return launch_lowm<1>(H, idx, rows, W, V, d, out, ldo, out_bf16, stream);

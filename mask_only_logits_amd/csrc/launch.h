@@ -18,15 +18,24 @@ enum LogitsVariant : int {
     kVariantF32 = 0,          // fp32 inputs: LDS-tiled FMA kernel
     kVariantBf16Tile256 = 1,  // bf16 inputs, d % 64 == 0: 256 x 256 MFMA tile, 2-stage LDS pipeline
     kVariantBf16Simple = 2,   // bf16 inputs, any d % 8 == 0: LDS-tiled FMA kernel
-    kVariantBf16K32S3 = 3,    // bf16, d % 32 == 0: 256 x 256 tile, K 32 deep, 3 LDS stages
+    kVariantBf16K32S3 = 3,    // bf16, d % 32 == 0: 256 x 256 tile, K 32 deep, 3 LDS stages (DMA over 2 sub-steps)
     kVariantBf16K32S4 = 4,    // ... 4 LDS stages
     kVariantBf16K32S5 = 5,    // ... 5 LDS stages (160 KiB)
     kVariantBf16LowM = 6,     // bf16, d % 64 == 0, M <= 64: W-streaming persistent kernel
-    kNumVariants = 7,
+    kVariantBf16K64Spread2 = 7,  // as 1, refill DMA spread over 2 k sub-steps
+    kVariantBf16K64Spread4 = 8,  // as 1, refill DMA spread over 4 k sub-steps
+    kVariantBf16PersistK64 = 9,    // persistent 256 x 256, BK 64, 2 stages, DMA over 2 sub-steps
+    kVariantBf16PersistK64S4 = 10, // ... DMA over 4 sub-steps
+    kVariantBf16PersistK32 = 11,   // persistent 256 x 256, BK 32, 4 stages
+    kNumVariants = 12,
 };
 
 // Default number of row tiles that share the W slabs of one XCD (tile order).
-constexpr int kDefaultGroupM = 4;
+constexpr int kDefaultGroupM = 8;
+
+// Launches of at most this many rows take the persistent BK-32 kernel; larger ones
+// the one-tile-per-workgroup BK-64 kernel (measured crossover on MI355X).
+constexpr int64_t kPersistMaxRows = 2048;
 
 // Whether a chunk of `rows` rows over V vocabulary rows fits the variant's launch grid.
 bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V);

@@ -67,7 +67,12 @@ bool variant_can_run(int v, int64_t M, int64_t d, mosaic_dtype_t in, mosaic_dtyp
     switch (v) {
     case mosaic::kVariantF32: return in == MOSAIC_F32 && out == MOSAIC_F32 && d % 4 == 0;
     case mosaic::kVariantBf16Simple: return bf16_in && d % 8 == 0;
-    case mosaic::kVariantBf16Tile256: return bf16_in && d % 64 == 0 && small_d;
+    case mosaic::kVariantBf16Tile256:
+    case mosaic::kVariantBf16K64Spread2:
+    case mosaic::kVariantBf16K64Spread4:
+    case mosaic::kVariantBf16PersistK64:
+    case mosaic::kVariantBf16PersistK64S4: return bf16_in && d % 64 == 0 && small_d;
+    case mosaic::kVariantBf16PersistK32: return bf16_in && d % 32 == 0 && small_d;
     case mosaic::kVariantBf16K32S3:
     case mosaic::kVariantBf16K32S4:
     case mosaic::kVariantBf16K32S5: return bf16_in && d % 32 == 0 && small_d;
@@ -84,10 +89,14 @@ int pick_variant(int64_t M, int64_t V, int64_t d, mosaic_dtype_t in, mosaic_dtyp
         return t.variant;
     if (variant_can_run(mosaic::kVariantF32, M, d, in, out))
         return mosaic::kVariantF32;
+    // Every bf16 variant below for one d accumulates each output in the same MFMA k
+    // order, so the choice (made per launch from its row count) never changes a bit.
     if (variant_can_run(mosaic::kVariantBf16LowM, M, d, in, out))
         return mosaic::kVariantBf16LowM;
-    if (variant_can_run(mosaic::kVariantBf16Tile256, M, d, in, out))
-        return mosaic::kVariantBf16Tile256;
+    if (M > mosaic::kPersistMaxRows && variant_can_run(mosaic::kVariantBf16K64Spread2, M, d, in, out))
+        return mosaic::kVariantBf16K64Spread2;
+    if (variant_can_run(mosaic::kVariantBf16PersistK32, M, d, in, out))
+        return mosaic::kVariantBf16PersistK32;
     if (variant_can_run(mosaic::kVariantBf16Simple, M, d, in, out))
         return mosaic::kVariantBf16Simple;
     return -1;
@@ -191,20 +200,27 @@ mosaic_status_t mosaic_masked_logits(const void *H, int64_t L, int64_t d, const 
         return MOSAIC_ERR_INVALID_ARG;
     if (L > kMaxPos || V > kMaxPos || d > kMaxPos)
         return MOSAIC_ERR_UNSUPPORTED;
-    const int variant = pick_variant(M, V, d, in_dtype, out_dtype);
-    if (variant < 0)
-        return MOSAIC_ERR_UNSUPPORTED;
-
-    // Row chunks ([k*C, min(M, (k+1)*C))), one launch each, same variant for all.
+    // Row chunks ([k*C, min(M, (k+1)*C))), one launch each.  All chunks run the variant
+    // chosen for C rows, except a last chunk small enough for the low-M streaming
+    // kernel; all chunks are checked before the first launch.
     const int64_t K = mosaic_num_chunks(M, chunk_rows);
     const int64_t C = (K == 1) ? M : chunk_rows;
-    if (C > kMaxPos || !mosaic::gather_gemm_grid_fits(variant, C, V))
+    const int64_t tail = M - (K - 1) * C;
+    if (C > kMaxPos)
+        return MOSAIC_ERR_UNSUPPORTED;
+    const int v_full = pick_variant(C, V, d, in_dtype, out_dtype);
+    int v_tail = pick_variant(tail, V, d, in_dtype, out_dtype);
+    if (v_tail != mosaic::kVariantBf16LowM)
+        v_tail = v_full;
+    if (v_full < 0 || v_tail < 0 || !mosaic::gather_gemm_grid_fits(v_full, C, V) ||
+        !mosaic::gather_gemm_grid_fits(v_tail, tail, V))
         return MOSAIC_ERR_UNSUPPORTED;
     const bool out_bf16 = out_dtype == MOSAIC_BF16;
     const int group_m = read_tune().group_m;
     for (int64_t k = 0; k < K; ++k) {
         const int64_t r0 = k * C;
         const int64_t r1 = (r0 + C < M) ? r0 + C : M;
+        const int variant = (r1 - r0 == C) ? v_full : v_tail;
         void *chunk_out = (char *)out + r0 * V * out_es;
         const hipError_t e = mosaic::launch_gather_gemm(variant, H, idx + r0, r1 - r0, W, V, d, chunk_out, V,
                                                         out_bf16, group_m, (hipStream_t)stream);

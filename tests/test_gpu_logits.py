@@ -41,7 +41,9 @@ CASES = [
     ("bf16", "bf16", 400, 192, 255, 255, 0),        # three K tiles (odd)
     ("bf16", "bf16", 300, 64, 3, 1, 0),             # a single row, tiny vocabulary
     ("bf16", "bf16", 300, 320, 513, 2, 0),
-    ("bf16", "bf16", 300, 72, 300, 100, 0),         # d % 64 != 0 kernel
+    ("bf16", "bf16", 300, 72, 300, 100, 0),         # d % 32 != 0 kernel
+    ("bf16", "bf16", 400, 96, 1000, 300, 0),        # d % 64 != 0, d % 32 == 0: persistent BK-32 kernel
+    ("bf16", "f32", 300, 160, 513, 70, 33),
     ("bf16", "bf16", 300, 8, 65, 33, 10),
     ("bf16", "f32", 700, 512, 1000, 600, 0),
     ("bf16", "f32", 300, 136, 129, 70, 0),
@@ -82,14 +84,15 @@ def test_parity_lowm(m, dt_out, L, d, V, M):
 
 
 @pytest.mark.parametrize("M,d,V,out", [(20, 3584, 5000, "bf16"), (64, 256, 1001, "f32"), (700, 512, 1000, "bf16"),
-                                       (1, 64, 300, "bf16")])
+                                       (1, 64, 300, "bf16"), (1000, 192, 40001, "bf16"), (777, 128, 30000, "f32"),
+                                       (600, 64, 70000, "bf16")])
 def test_bf16_variants_bit_identical(m, monkeypatch, M, d, V, out):
     # every bf16 MFMA variant accumulates each output in the same MFMA k order
     wl = inputs.make_random(M + d + V, L=max(M, 300), d=d, V=V, M=M, dtype="bf16")
     _, idx_d = _gpu_idx(wl)
     H, W = wl.H.to(DEV), wl.W.to(DEV)
     ref = m.mosaic_masked_logits(H, idx_d, W, out_dtype=TD[out])
-    for v in (1, 3, 4, 5, 6):
+    for v in (1, 3, 4, 5, 6, 7, 8, 9, 10, 11):
         if v == 6 and M > 64:
             continue
         monkeypatch.setenv("MOSAIC_TUNE", f"variant={v}")
@@ -140,7 +143,7 @@ def test_chunked_equals_unchunked_bit_exact(m, dt):
     _, idx_d = _gpu_idx(wl)
     H, W = wl.H.to(DEV), wl.W.to(DEV)
     ref = m.mosaic_masked_logits(H, idx_d, W)
-    for C in (1, 63, 64, 255, 256, 257, 1000, 1099, 1100, 5000, -1):
+    for C in (1, 63, 64, 255, 256, 257, 259, 1000, 1040, 1099, 1100, 5000, -1):   # 259, 1040: low-M last chunk
         got = m.mosaic_masked_logits(H, idx_d, W, chunk_rows=C)
         assert torch.equal(got, ref), C
     # streaming use: one call per chunk into a reused buffer
