@@ -91,22 +91,24 @@ __device__ __forceinline__ int swz(int r)
         return (r >> 2) & 3;                      // 4 chunks per row; rows r, r+4, r+8, r+12
 }
 
-template <int BV, int BM, int BK, int NSTAGE, int NSPREAD, bool OUT_BF16>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
+template <int BV, int BM, int BK, int NSTAGE, int NSPREAD, int NW, bool OUT_BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW / 4, NW / 4))) void
 gather_gemm_bf16_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict__ idx, int32_t rows,
                         const __bf16 *__restrict__ W, int32_t V, int32_t d, void *__restrict__ out,
                         int64_t ldo, int32_t group_m)
 {
     static_assert(BK == 32 || BK == 64, "BK");
+    static_assert(NW == 4 || NW == 8, "waves");
     constexpr int ROW_BYTES = BK * 2;         // 64 or 128
     constexpr int CHUNKS = BK / 8;            // 16-byte chunks per row
     constexpr int RPI = 64 / CHUNKS;          // tile rows filled by one 64-lane DMA instruction
     constexpr int W_TILE = BV * ROW_BYTES;
     constexpr int H_TILE = BM * ROW_BYTES;
     constexpr int STAGE = W_TILE + H_TILE;
-    constexpr int WV = BV / 2, WM = BM / 2;   // wave sub-tile (2 x 2 waves)
+    // wave sub-tile: 2 waves along V x NW/2 along M (one or two waves per SIMD)
+    constexpr int WV = BV / 2, WM = BM / (NW / 2);
     constexpr int AV = WV / 32, AM = WM / 32; // 32 x 32 MFMA blocks per wave
-    constexpr int LW = BV / RPI / 4, LH = BM / RPI / 4;   // DMA instructions per wave and K tile
+    constexpr int LW = BV / RPI / NW, LH = BM / RPI / NW;   // DMA instructions per wave and K tile
     constexpr int NSUB = BK / 16;             // MFMA k sub-steps per K tile
     static_assert(AV >= 1 && AM >= 1 && LW >= 1 && LH >= 1, "tile too small");
     static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS");
@@ -697,6 +699,326 @@ gather_gemm_bf16_persist_kernel(const __bf16 *__restrict__ H, const int32_t *__r
     }
 }
 
+// Persistent eight-wave form with deferred stores (bf16 output).
+//  * 256 x 256 tiles, K staged 64 deep in two LDS stages, eight waves: two per SIMD, so
+//    while one wave waits (DMA issue, barrier) the other keeps the matrix core busy.  A
+//    wave owns 128 vocabulary x 64 masked rows (4 x 2 MFMA blocks, 128 accumulators).
+//  * Tile list per XCD as in the persistent kernel above.
+//  * When a tile's K loop ends, its results are rounded to bf16 and arranged for 16-byte
+//    stores (permlane32_swap) in registers; NIMM of its stores go out at once and the rest
+//    are issued over the first DEFER K steps of the next tile.  Every workgroup reaches a
+//    tile boundary at about the same time, so storing whole tiles there sends one burst of
+//    all workgroups' results to memory while the matrix cores idle; spreading the stores
+//    over MFMA time removes most of that cost.  The last tile stores at once.
+// Same MFMA, operand roles and k order as the tiled kernel: results are bit-identical.
+template <int NSPREAD, int DEFER, int NIMM>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
+gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict__ idx, int32_t rows,
+                              const __bf16 *__restrict__ W, int32_t V, int32_t d, __bf16 *__restrict__ out,
+                              int64_t ldo, int32_t group_m)
+{
+    constexpr int NW = 8, BV = 256, BM = 256, BK = 64, NSTAGE = 2;
+    constexpr int ROW_BYTES = BK * 2;
+    constexpr int CHUNKS = BK / 8;
+    constexpr int RPI = 64 / CHUNKS;
+    constexpr int W_TILE = BV * ROW_BYTES;
+    constexpr int H_TILE = BM * ROW_BYTES;
+    constexpr int STAGE = W_TILE + H_TILE;
+    constexpr int WV = BV / 2, WM = BM / (NW / 2);
+    constexpr int AV = WV / 32, AM = WM / 32;
+    constexpr int LW = BV / RPI / NW, LH = BM / RPI / NW;
+    constexpr int NSUB = BK / 16;
+    constexpr int NDMA = LW + LH;
+    constexpr int NFR = AV + AM;
+    constexpr int NST = AV * AM * 2;          // 16-byte stores per lane and tile
+    static_assert(NSPREAD >= 1 && NSPREAD <= NSUB && NDMA % NSPREAD == 0, "spread");
+    static_assert(NIMM >= 0 && NIMM <= NST && DEFER >= 1 && (NST - NIMM) % DEFER == 0, "defer");
+    constexpr int PER = NDMA / NSPREAD;
+    constexpr int SPS = (NST - NIMM) / DEFER; // deferred stores per K step
+
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+
+    const int nvt = (V + BV - 1) / BV;
+    const int nmt = (rows + BM - 1) / BM;
+    const int ntiles = nvt * nmt;
+    const int nk = d / BK;
+
+    // ---- this workgroup's tile list
+    const int G = gridDim.x;                    // a multiple of 8
+    const int per_xcd = G >> 3;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int q = ntiles >> 3, rem = ntiles & 7;
+    const int start = xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q;
+    const int count = q + (xcd < rem ? 1 : 0);
+    const int n_my = slot < count ? (count - slot + per_xcd - 1) / per_xcd : 0;
+    if (n_my == 0)
+        return;
+    auto tile_coords = [&](int i, int &m0, int &v0) {
+        const int t = start + slot + i * per_xcd;
+        const int per_group = group_m * nvt;
+        const int g = t / per_group;
+        const int first_m = g * group_m;
+        const int gsz = min(nmt - first_m, group_m);
+        const int local = t - g * per_group;
+        m0 = (first_m + local % gsz) * BM;
+        v0 = (local / gsz) * BV;
+    };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wv = wave & 1, wm = wave >> 1;
+
+    // ---- DMA sources of the current tile (same layout as the tiled kernel)
+    auto row_w = [&](int j) { return (wave * LW + j) * RPI + lane / CHUNKS; };
+    auto row_h = [&](int j) { return (wave * LH + j) * RPI + lane / CHUNKS; };
+    auto chunk_of = [&](int r) { return ((lane % CHUNKS) ^ swz<BK>(r)) * 16; };
+    int32_t hidx_nxt[LH];                       // H row ids of the next tile (loaded a tile ahead)
+    auto load_hidx = [&](int i) {
+        if (i >= n_my)
+            return;
+        int m0, v0;
+        tile_coords(i, m0, v0);
+#pragma unroll
+        for (int j = 0; j < LH; ++j)
+            hidx_nxt[j] = idx[min(m0 + row_h(j), rows - 1)];
+    };
+    const char *wbase;
+    uint32_t woff[LW];
+    const char *hsrc[LH];
+    auto make_src = [&](int i) {
+        int m0, v0;
+        tile_coords(i, m0, v0);
+        wbase = (const char *)(W + (int64_t)v0 * d);
+#pragma unroll
+        for (int j = 0; j < LW; ++j) {
+            const int vr = min(v0 + row_w(j), V - 1) - v0;
+            woff[j] = (uint32_t)vr * (uint32_t)d * 2u + (uint32_t)chunk_of(row_w(j));
+        }
+#pragma unroll
+        for (int j = 0; j < LH; ++j)
+            hsrc[j] = (const char *)(H + (int64_t)hidx_nxt[j] * d) + chunk_of(row_h(j));
+    };
+    load_hidx(0);
+    make_src(0);
+    load_hidx(1);
+
+    auto issue_part = [&](int so, int kt, int p) {
+        const int kb = kt * ROW_BYTES;
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            if (i / PER != p)
+                continue;
+            if (i < LW)
+                __builtin_amdgcn_global_load_lds((const void *)(wbase + kb + woff[i]),
+                                                 (lds_void_t *)(smem + so + (wave * LW + i) * 1024), 16, 0, 0);
+            else
+                __builtin_amdgcn_global_load_lds((const void *)(hsrc[i - LW] + kb),
+                                                 (lds_void_t *)(smem + so + W_TILE + (wave * LH + i - LW) * 1024),
+                                                 16, 0, 0);
+        }
+    };
+
+    f32x16_t acc[AV][AM];
+#pragma unroll
+    for (int a = 0; a < AV; ++a)
+#pragma unroll
+        for (int bm = 0; bm < AM; ++bm)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[a][bm][e] = 0.0f;
+
+    const int fr = lane & 31, hi = lane >> 5;
+    const int lane_chunk = (hi ^ swz<BK>(fr)) * 16;
+    const int a_addr = (wv * WV + fr) * ROW_BYTES + lane_chunk;
+    const int b_addr = W_TILE + (wm * WM + fr) * ROW_BYTES + lane_chunk;
+
+    auto load_frags = [&](int so, int s, bf16x8_t (&af)[AV], bf16x8_t (&bf)[AM]) {
+        const int ab = (a_addr + so) ^ (32 * s), bb = (b_addr + so) ^ (32 * s);
+#pragma unroll
+        for (int a = 0; a < AV; ++a)
+            af[a] = *(const bf16x8_t *)(smem + ab + a * 32 * ROW_BYTES);
+#pragma unroll
+        for (int bm = 0; bm < AM; ++bm)
+            bf[bm] = *(const bf16x8_t *)(smem + bb + bm * 32 * ROW_BYTES);
+    };
+    auto mma = [&](const bf16x8_t (&af)[AV], const bf16x8_t (&bf)[AM]) {
+#pragma unroll
+        for (int a = 0; a < AV; ++a)
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm)
+                acc[a][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bf[bm], acc[a][bm], 0, 0, 0);
+    };
+    auto interleave = [&](int nvm) {
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            if (i < nvm) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NFR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+
+    // ---- results of the previous tile, as 16-byte store words: store j covers block
+    // (a, bm) = ((j / 2) / AM, (j / 2) % AM), vocabulary entries 16 * (j % 2) + 8 * hi + (0..7)
+    // of that block for masked row 32 * bm + fr of the wave's sub-tile.
+    uint32_t pk[NST][4];
+    int pm0 = 0, pv0 = 0;
+    const bool vec_ok = ((uintptr_t)out & 15) == 0 && (ldo & 7) == 0;
+    auto store_one = [&](int j) {
+        const int a = (j >> 1) / AM, bm = (j >> 1) % AM, pr = j & 1;
+        const int row = pm0 + wm * WM + bm * 32 + fr;
+        const int v = pv0 + wv * WV + a * 32 + 16 * pr + 8 * hi;
+        if (row < rows) {
+            __bf16 *o = out + (int64_t)row * ldo + v;
+            if (vec_ok && v + 7 < V) {
+                *(uint4 *)o = make_uint4(pk[j][0], pk[j][1], pk[j][2], pk[j][3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (v + e < V)
+                        o[e] = __builtin_bit_cast(__bf16, (uint16_t)(pk[j][e >> 1] >> (16 * (e & 1))));
+            }
+        }
+    };
+    // acc -> pk (round to bf16; lanes 0-31 take entries 0-7 / 16-23 of a block, lanes 32-63
+    // entries 8-15 / 24-31), then restart the accumulators
+    auto pack = [&]() {
+#pragma unroll
+        for (int a = 0; a < AV; ++a)
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm) {
+                uint32_t p[4][2];
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    p[gq][0] = pack_bf16x2(acc[a][bm][gq * 4 + 0], acc[a][bm][gq * 4 + 1]);
+                    p[gq][1] = pack_bf16x2(acc[a][bm][gq * 4 + 2], acc[a][bm][gq * 4 + 3]);
+                }
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const auto s0 = __builtin_amdgcn_permlane32_swap(p[2 * pr][0], p[2 * pr + 1][0], false, false);
+                    const auto s1 = __builtin_amdgcn_permlane32_swap(p[2 * pr][1], p[2 * pr + 1][1], false, false);
+                    const int j = (a * AM + bm) * 2 + pr;
+                    pk[j][0] = s0[0];
+                    pk[j][1] = s1[0];
+                    pk[j][2] = s0[1];
+                    pk[j][3] = s1[1];
+                }
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[a][bm][e] = 0.0f;
+            }
+    };
+
+    bf16x8_t af[2][AV], bf[2][AM];
+    const int npre = min(NSTAGE, nk);
+    for (int s = 0; s < npre; ++s)
+#pragma unroll
+        for (int p = 0; p < NSPREAD; ++p)
+            issue_part(s * STAGE, s, p);
+
+    for (int i = 0; i < n_my; ++i) {
+        if (npre == 2)
+            wait_vmcnt<NDMA>();
+        else
+            wait_vmcnt<0>();
+        barrier_no_fence();
+        load_frags(0, 0, af[0], bf[0]);
+        int rd = 0, pso = 0, pkt = 0, kt = 0;
+        bool pending = false;
+        // One step of the steady state (as in the tiled kernel); `hook` issues the deferred
+        // stores of this step in its second k sub-step.  Every step ends with vmcnt(0), so
+        // the stores are complete before the step's barrier, like the DMA.
+        auto steady = [&](auto hook) {
+#pragma unroll
+            for (int s = 0; s + 1 < NSUB; ++s) {
+                if (s + 1 < NSPREAD && pending)
+                    issue_part(pso, pkt, s + 1);
+                if (s == 1)
+                    hook();
+                load_frags(rd, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+                mma(af[s & 1], bf[s & 1]);
+                interleave(s + 1 < NSPREAD ? PER : 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            wait_vmcnt<0>();
+            barrier_no_fence();
+            __builtin_amdgcn_sched_barrier(0);
+            issue_part(rd, kt + NSTAGE, 0);
+            pso = rd;
+            pkt = kt + NSTAGE;
+            pending = NSPREAD > 1;
+            const int nx = (rd + STAGE == NSTAGE * STAGE) ? 0 : rd + STAGE;
+            load_frags(nx, 0, af[NSUB & 1], bf[NSUB & 1]);
+            mma(af[(NSUB - 1) & 1], bf[(NSUB - 1) & 1]);
+            interleave(PER);
+            __builtin_amdgcn_sched_barrier(0);
+            rd = nx;
+            ++kt;
+        };
+        if (i > 0 && SPS > 0) {
+            if (nk >= NSTAGE + DEFER) {
+#pragma unroll
+                for (int j = 0; j < DEFER; ++j)
+                    steady([&] {
+#pragma unroll
+                        for (int q2 = 0; q2 < SPS; ++q2)
+                            store_one(NIMM + j * SPS + q2);
+                    });
+            } else {
+#pragma unroll
+                for (int j = NIMM; j < NST; ++j)
+                    store_one(j);
+            }
+        }
+        while (kt + NSTAGE < nk)
+            steady([] {});
+        for (; kt < nk; ++kt) {
+#pragma unroll
+            for (int s = 0; s + 1 < NSUB; ++s) {
+                if (s + 1 < NSPREAD && pending)
+                    issue_part(pso, pkt, s + 1);
+                load_frags(rd, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+                mma(af[s & 1], bf[s & 1]);
+            }
+            pending = false;
+            if (kt + 1 < nk) {
+                wait_vmcnt<0>();
+                barrier_no_fence();
+                rd = (rd + STAGE == NSTAGE * STAGE) ? 0 : rd + STAGE;
+                load_frags(rd, 0, af[NSUB & 1], bf[NSUB & 1]);
+            }
+            mma(af[(NSUB - 1) & 1], bf[(NSUB - 1) & 1]);
+        }
+        // every wave's last fragments are in registers: the stages are free
+        wait_vmcnt<63>();
+        barrier_no_fence();
+        if (i + 1 < n_my) {
+            make_src(i + 1);
+            for (int s = 0; s < npre; ++s)
+#pragma unroll
+                for (int p = 0; p < NSPREAD; ++p)
+                    issue_part(s * STAGE, s, p);
+        }
+        tile_coords(i, pm0, pv0);
+        pack();
+#pragma unroll
+        for (int j = 0; j < NIMM; ++j)
+            store_one(j);
+        if (i + 1 == n_my) {
+#pragma unroll
+            for (int j = NIMM; j < NST; ++j)
+                store_one(j);
+        }
+        load_hidx(i + 2);
+    }
+}
+
 // Low-M gather-GEMM (M <= 32 * AM): the work is streaming W once from HBM.
 //
 // Every wave is an independent stream.  Wave w of the grid owns an equal, contiguous
@@ -983,20 +1305,20 @@ __global__ __launch_bounds__(256) void gather_gemm_f32_kernel(const float *__res
     }
 }
 
-template <int BV, int BM, int BK, int NSTAGE, int NSPREAD = 1>
+template <int BV, int BM, int BK, int NSTAGE, int NSPREAD = 1, int NW = 4>
 hipError_t launch_bf16(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V, int64_t d,
                        void *out, int64_t ldo, bool out_bf16, int group_m, hipStream_t stream)
 {
     const int64_t nvt = (V + BV - 1) / BV, nmt = (rows + BM - 1) / BM;
     const dim3 grid((unsigned)(nvt * nmt));
     if (out_bf16)
-        hipLaunchKernelGGL((gather_gemm_bf16_kernel<BV, BM, BK, NSTAGE, NSPREAD, true>), grid, dim3(256), 0, stream,
-                           (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d, out,
-                           ldo, group_m);
+        hipLaunchKernelGGL((gather_gemm_bf16_kernel<BV, BM, BK, NSTAGE, NSPREAD, NW, true>), grid, dim3(64 * NW), 0,
+                           stream, (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d,
+                           out, ldo, group_m);
     else
-        hipLaunchKernelGGL((gather_gemm_bf16_kernel<BV, BM, BK, NSTAGE, NSPREAD, false>), grid, dim3(256), 0, stream,
-                           (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d, out,
-                           ldo, group_m);
+        hipLaunchKernelGGL((gather_gemm_bf16_kernel<BV, BM, BK, NSTAGE, NSPREAD, NW, false>), grid, dim3(64 * NW), 0,
+                           stream, (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d,
+                           out, ldo, group_m);
     return hipGetLastError();
 }
 
@@ -1019,6 +1341,22 @@ hipError_t launch_persist(const void *H, const int32_t *idx, int64_t rows, const
         hipLaunchKernelGGL((gather_gemm_bf16_persist_kernel<BK, NSTAGE, NSPREAD, false>), dim3((unsigned)grid), dim3(256),
                            0, stream, (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d,
                            out, ldo, group_m);
+    return hipGetLastError();
+}
+
+template <int NSPREAD, int DEFER, int NIMM>
+hipError_t launch_defer(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V, int64_t d,
+                        void *out, int64_t ldo, int group_m, hipStream_t stream)
+{
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t ntiles = ((V + 255) / 256) * ((rows + 255) / 256);
+    int64_t grid = std::max<int64_t>(8, (cus / 8) * 8);
+    grid = std::min<int64_t>(grid, ((ntiles + 7) / 8) * 8);
+    hipLaunchKernelGGL((gather_gemm_bf16_defer_kernel<NSPREAD, DEFER, NIMM>), dim3((unsigned)grid), dim3(512), 0,
+                       stream, (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d,
+                       (__bf16 *)out, ldo, group_m);
     return hipGetLastError();
 }
 
@@ -1058,6 +1396,12 @@ bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V)
     case kVariantBf16PersistK64:
     case kVariantBf16PersistK64S4:
     case kVariantBf16PersistK32:
+    case kVariantBf16W8K64S2:
+    case kVariantBf16W8K64:
+    case kVariantBf16W8K32S4:
+    case kVariantBf16DeferS8:
+    case kVariantBf16DeferS4I8:
+    case kVariantBf16DeferS16:
         return ((rows + 255) / 256) * ((V + 255) / 256) <= 0x7fffffffLL;
     case kVariantBf16LowM:
         return rows <= 64;
@@ -1101,6 +1445,18 @@ hipError_t launch_gather_gemm(int variant, const void *H, const int32_t *idx, in
         return launch_bf16<256, 256, 64, 2, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
     case kVariantBf16K64Spread4:
         return launch_bf16<256, 256, 64, 2, 4>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
+    case kVariantBf16W8K64S2:
+        return launch_bf16<256, 256, 64, 2, 2, 8>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
+    case kVariantBf16W8K64:
+        return launch_bf16<256, 256, 64, 2, 1, 8>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
+    case kVariantBf16W8K32S4:
+        return launch_bf16<256, 256, 32, 4, 2, 8>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
+    case kVariantBf16DeferS8:
+        return out_bf16 ? launch_defer<2, 8, 0>(H, idx, rows, W, V, d, out, ldo, group_m, stream) : hipErrorInvalidValue;
+    case kVariantBf16DeferS4I8:
+        return out_bf16 ? launch_defer<2, 4, 8>(H, idx, rows, W, V, d, out, ldo, group_m, stream) : hipErrorInvalidValue;
+    case kVariantBf16DeferS16:
+        return out_bf16 ? launch_defer<2, 16, 0>(H, idx, rows, W, V, d, out, ldo, group_m, stream) : hipErrorInvalidValue;
     case kVariantBf16PersistK64:
         return launch_persist<64, 2, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
     case kVariantBf16PersistK64S4:

@@ -27,15 +27,18 @@ enum LogitsVariant : int {
     kVariantBf16PersistK64 = 9,    // persistent 256 x 256, BK 64, 2 stages, DMA over 2 sub-steps
     kVariantBf16PersistK64S4 = 10, // ... DMA over 4 sub-steps
     kVariantBf16PersistK32 = 11,   // persistent 256 x 256, BK 32, 4 stages
-    kNumVariants = 12,
+    kVariantBf16W8K64S2 = 12,      // 256 x 256, 8 waves (2 per SIMD), BK 64, DMA over 2 sub-steps
+    kVariantBf16W8K64 = 13,        // ... refill DMA in one sub-step
+    kVariantBf16W8K32S4 = 14,      // 256 x 256, 8 waves, BK 32, 4 stages
+    kVariantBf16DeferS8 = 15,      // persistent 8-wave, bf16 out, tile stores spread over 8 K steps
+    kVariantBf16DeferS4I8 = 16,    // ... half the stores at once, half over 4 K steps
+    kVariantBf16DeferS16 = 17,     // ... stores spread over 16 K steps
+    kNumVariants = 18,
 };
 
 // Default number of row tiles that share the W slabs of one XCD (tile order).
 constexpr int kDefaultGroupM = 8;
 
-// Launches of at most this many rows take the persistent BK-32 kernel; larger ones
-// the one-tile-per-workgroup BK-64 kernel (measured crossover on MI355X).
-constexpr int64_t kPersistMaxRows = 2048;
 
 // Whether a chunk of `rows` rows over V vocabulary rows fits the variant's launch grid.
 bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V);

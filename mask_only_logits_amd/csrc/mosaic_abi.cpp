@@ -71,7 +71,13 @@ bool variant_can_run(int v, int64_t M, int64_t d, mosaic_dtype_t in, mosaic_dtyp
     case mosaic::kVariantBf16K64Spread2:
     case mosaic::kVariantBf16K64Spread4:
     case mosaic::kVariantBf16PersistK64:
-    case mosaic::kVariantBf16PersistK64S4: return bf16_in && d % 64 == 0 && small_d;
+    case mosaic::kVariantBf16PersistK64S4:
+    case mosaic::kVariantBf16W8K64S2:
+    case mosaic::kVariantBf16W8K64: return bf16_in && d % 64 == 0 && small_d;
+    case mosaic::kVariantBf16DeferS8:
+    case mosaic::kVariantBf16DeferS4I8:
+    case mosaic::kVariantBf16DeferS16: return in == MOSAIC_BF16 && out == MOSAIC_BF16 && d % 64 == 0 && small_d;
+    case mosaic::kVariantBf16W8K32S4:
     case mosaic::kVariantBf16PersistK32: return bf16_in && d % 32 == 0 && small_d;
     case mosaic::kVariantBf16K32S3:
     case mosaic::kVariantBf16K32S4:
@@ -93,8 +99,10 @@ int pick_variant(int64_t M, int64_t V, int64_t d, mosaic_dtype_t in, mosaic_dtyp
     // order, so the choice (made per launch from its row count) never changes a bit.
     if (variant_can_run(mosaic::kVariantBf16LowM, M, d, in, out))
         return mosaic::kVariantBf16LowM;
-    if (M > mosaic::kPersistMaxRows && variant_can_run(mosaic::kVariantBf16K64Spread2, M, d, in, out))
-        return mosaic::kVariantBf16K64Spread2;
+    if (variant_can_run(mosaic::kVariantBf16DeferS4I8, M, d, in, out))
+        return mosaic::kVariantBf16DeferS4I8;
+    if (variant_can_run(mosaic::kVariantBf16W8K64S2, M, d, in, out))
+        return mosaic::kVariantBf16W8K64S2;
     if (variant_can_run(mosaic::kVariantBf16PersistK32, M, d, in, out))
         return mosaic::kVariantBf16PersistK32;
     if (variant_can_run(mosaic::kVariantBf16Simple, M, d, in, out))

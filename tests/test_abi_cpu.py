@@ -57,14 +57,13 @@ def test_logits_bytes(m):
 def test_variant_choice(m):
     import torch
     bf, f32 = torch.bfloat16, torch.float32
-    assert m.mosaic_logits_variant(4096, 126464, 4096, bf, bf) == 7      # tiled BK-64 kernel
-    assert m.mosaic_logits_variant(2049, 126464, 4096, bf, bf) == 7
-    assert m.mosaic_logits_variant(2048, 126464, 4096, bf, bf) == 11     # persistent BK-32 kernel
+    assert m.mosaic_logits_variant(4096, 126464, 4096, bf, bf) == 16     # persistent, deferred stores
+    assert m.mosaic_logits_variant(65, 152064, 3584, bf, bf) == 16
+    assert m.mosaic_logits_variant(4096, 126464, 4096, bf, f32) == 12    # 8-wave tiled kernel
     assert m.mosaic_logits_variant(20, 152064, 3584, bf, bf) == 6        # low-M streaming kernel
     assert m.mosaic_logits_variant(64, 152064, 3584, bf, f32) == 6
-    assert m.mosaic_logits_variant(65, 152064, 3584, bf, bf) == 11
     assert m.mosaic_logits_variant(20, 1000, 96, bf, bf) == 11           # d % 32 == 0 only
-    assert m.mosaic_logits_variant(5000, 1000, 96, bf, bf) == 11
+    assert m.mosaic_logits_variant(5000, 1000, 96, bf, f32) == 11
     assert m.mosaic_logits_variant(128, 1024, 256, f32, f32) == 0
     assert m.mosaic_logits_variant(10, 10, 72, bf, f32) == 2          # d % 64 != 0
     assert m.mosaic_logits_variant(10, 10, 12, bf, bf) == -1          # d % 8 != 0

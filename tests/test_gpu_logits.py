@@ -85,14 +85,14 @@ def test_parity_lowm(m, dt_out, L, d, V, M):
 
 @pytest.mark.parametrize("M,d,V,out", [(20, 3584, 5000, "bf16"), (64, 256, 1001, "f32"), (700, 512, 1000, "bf16"),
                                        (1, 64, 300, "bf16"), (1000, 192, 40001, "bf16"), (777, 128, 30000, "f32"),
-                                       (600, 64, 70000, "bf16")])
+                                       (600, 64, 70000, "bf16"), (600, 1280, 70000, "bf16")])
 def test_bf16_variants_bit_identical(m, monkeypatch, M, d, V, out):
     # every bf16 MFMA variant accumulates each output in the same MFMA k order
     wl = inputs.make_random(M + d + V, L=max(M, 300), d=d, V=V, M=M, dtype="bf16")
     _, idx_d = _gpu_idx(wl)
     H, W = wl.H.to(DEV), wl.W.to(DEV)
     ref = m.mosaic_masked_logits(H, idx_d, W, out_dtype=TD[out])
-    for v in (1, 3, 4, 5, 6, 7, 8, 9, 10, 11):
+    for v in (1, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17):
         if v == 6 and M > 64:
             continue
         monkeypatch.setenv("MOSAIC_TUNE", f"variant={v}")
