@@ -10,9 +10,10 @@
 // gfx950 design (bf16 path):
 //  * Tile: 256 vocabulary rows x 256 masked rows per workgroup, K staged 64 deep
 //    (128 bytes per row).  Four waves, each owning a 128 x 128 sub-tile as 4 x 4 blocks
-//    of v_mfma_f32_32x32x16_bf16 (fp32 accumulators: 256 per lane).  W is the MFMA
-//    A operand (vocabulary rows) and the gathered H rows are the B operand, so each
-//    lane's accumulators hold four consecutive vocabulary entries of one masked row.
+//    of v_mfma_f32_32x32x16_bf16 (fp32 accumulators: 256 per lane), or eight waves (two
+//    per SIMD) of 128 x 64.  W is the MFMA A operand (vocabulary rows) and the gathered
+//    H rows are the B operand, so each lane's accumulators hold four consecutive
+//    vocabulary entries of one masked row.
 //  * Operands reach LDS with global_load_lds_dwordx4 (16 bytes per lane, written to
 //    LDS without passing through VGPRs).  The gather is free: each lane's source
 //    address is just H + idx[row] * d + k, and a 64-lane instruction fills 8 rows x
@@ -29,6 +30,9 @@
 //  * Bit-identity across chunks: every output element is one accumulation chain over
 //    k = 0, 16, 32, ... in the same MFMA positions whatever the chunk, tile or row
 //    position, so splitting the rows into chunks never changes a bit.
+//  * Variants of this design (one tile per workgroup; persistent per-XCD tile lists;
+//    deferred epilogue stores) and a low-M streaming kernel share the MFMA, operand
+//    roles and k order, so they all produce identical bits.
 //
 // fp32 path (small fp32 problems): an LDS-tiled FMA kernel, 64 x 64 outputs per
 // workgroup, fp32 accumulation in ascending k.
