@@ -34,7 +34,7 @@ def build(force: bool = True) -> Path:
     if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
         tmp = _LIB.with_suffix(".so.tmp")
         cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
-               "-Wall", "-Wextra", "-o", str(tmp), str(_SRC)]
+               "-Wall", "-Wextra", "-o", str(tmp), str(_SRC), "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -62,6 +62,9 @@ def _load():
             f.argtypes = [_p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
         lib.oracle_masked_logits_chunked_bf16.restype = ctypes.c_int
         lib.oracle_masked_logits_chunked_bf16.argtypes = [_p, _i64, _i64, _p, _i64, _p, _i64, _i64, _p]
+        lib.oracle_masked_logits_argmax_lse_bf16.restype = ctypes.c_int
+        lib.oracle_masked_logits_argmax_lse_bf16.argtypes = [_p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
+                                                             _p, _p, _p]
         lib.oracle_logits_bytes.restype = _i64
         lib.oracle_logits_bytes.argtypes = [_i64, _i64, _i64]
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -166,6 +169,31 @@ def masked_logits(H, idx, W, rows=None) -> np.ndarray:
     if rc != 0:
         raise IndexError("row or index out of range")
     return out
+
+
+def masked_logits_argmax_lse(H, idx, W, rows=None):
+    """Per-row consumer of the bf16 masked logits: (row_max fp64, row_argmax int64,
+    row_lse fp64) for output rows `rows` (default: all M rows)."""
+    h = _np(H, np.uint16)
+    w = _np(W, np.uint16)
+    L, d = h.shape
+    V = w.shape[0]
+    assert w.shape[1] == d
+    ix = _np(idx, np.int32)
+    M = ix.size
+    r = np.arange(M, dtype=np.int64) if rows is None else _np(rows, np.int64)
+    mx = np.empty(r.size, np.float64)
+    am = np.empty(r.size, np.int64)
+    lse = np.empty(r.size, np.float64)
+    if r.size == 0:
+        return mx, am, lse
+    rc = _load().oracle_masked_logits_argmax_lse_bf16(_ptr(h), L, d, _ptr(ix), M, _ptr(w), V, _ptr(r), r.size,
+                                                      _ptr(mx), _ptr(am), _ptr(lse))
+    if rc == -1:
+        raise IndexError("row or index out of range")
+    if rc != 0:
+        raise ValueError("empty vocabulary or out of memory")
+    return mx, am, lse
 
 
 def masked_logits_chunked(H, idx, W, chunk_rows: int) -> np.ndarray:

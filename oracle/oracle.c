@@ -28,10 +28,22 @@
  *      or two fp32 values are exact in fp64).  No bias, scale or softcap: the pages
  *      name only the lm_head projection.
  *
- * Parallelism: OpenMP over output elements.  It does not change any arithmetic;
- * every element is still one ascending-k fp64 sum.
+ *  (4) per-row consumer -- what the sampler reads from a masked row's logits z[v]:
+ *      the largest logit, the first vocabulary index that attains it (greedy
+ *      decoding), and log(sum_v exp z[v]), from which the softmax confidence of any
+ *      token follows.  The pages say only that the masked tokens' logits are sampled
+ *      (Mosaic review, 核心观察 #2) and that a micro-batch's logits can be freed as
+ *      soon as they are consumed ("扩散大语言模型内存优化：从理论到系统设计", §3.2.3);
+ *      they do not define the sampler, so these three reductions are the plainest
+ *      reading.  The logits are (3)'s fp64 values; the log-sum-exp subtracts the
+ *      maximum before exponentiating (the textbook stable form) and uses libm exp/log.
+ *
+ * Parallelism: OpenMP over output elements (rows for (4)).  It does not change any
+ * arithmetic; every element is still one ascending-k fp64 sum.
  */
+#include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ---------------------------------------------------------------- (1) compaction */
@@ -186,6 +198,55 @@ int oracle_masked_logits_chunked_bf16(const uint16_t *H, int64_t L, int64_t d, c
         }
     }
     return 0;
+}
+
+/* ------------------------------------------------------- (4) per-row consumer */
+
+/* For each output row rows[r] (an index into idx[0..M)): its logits z[v] = (3) for
+ * v < V, then
+ *   row_max[r]    = max_v z[v]
+ *   row_argmax[r] = the smallest v with z[v] == row_max[r]
+ *   row_lse[r]    = row_max[r] + log(sum_v exp(z[v] - row_max[r])).
+ * bf16 H and W as in (3).  V must be >= 1.  Returns 0, -1 for an index out of range,
+ * -2 when V < 1 or a row buffer cannot be allocated. */
+int oracle_masked_logits_argmax_lse_bf16(const uint16_t *H, int64_t L, int64_t d, const int32_t *idx,
+                                         int64_t M, const uint16_t *W, int64_t V, const int64_t *rows,
+                                         int64_t nrows, double *row_max, int64_t *row_argmax,
+                                         double *row_lse)
+{
+    if (V < 1)
+        return -2;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= M || idx[rows[r]] < 0 || idx[rows[r]] >= L)
+            return -1;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        double *z = (double *)malloc((size_t)V * sizeof(double));
+        if (!z) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        const uint16_t *h_row = H + (int64_t)idx[rows[r]] * d;
+        for (int64_t v = 0; v < V; ++v)
+            z[v] = lm_head_dot_bf16(h_row, W + v * d, d);
+        double m = z[0];
+        int64_t am = 0;
+        for (int64_t v = 1; v < V; ++v)
+            if (z[v] > m) {
+                m = z[v];
+                am = v;
+            }
+        double s = 0.0;
+        for (int64_t v = 0; v < V; ++v)
+            s += exp(z[v] - m);
+        row_max[r] = m;
+        row_argmax[r] = am;
+        row_lse[r] = m + log(s);
+        free(z);
+    }
+    return failed ? -2 : 0;
 }
 
 /* Number of OpenMP threads the logits loops run on (1 when built without OpenMP). */
