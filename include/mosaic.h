@@ -127,6 +127,46 @@ mosaic_status_t mosaic_masked_logits(const void *H, int64_t L, int64_t d,
                                      mosaic_dtype_t in_dtype, mosaic_dtype_t out_dtype,
                                      void *stream);
 
+/* ------------------------------------------------------- per-row consumer --- */
+
+/* The sampler's view of each masked row, reduced inside the logits kernel so a row's
+ * logits are consumed as they are produced ([MR] 核心观察 #2: only masked tokens are
+ * sampled; [DS] §3.2.3: a micro-batch's logits can be freed once consumed).  The pages
+ * do not define the sampler; these are the plainest per-row quantities it needs
+ * (greedy choice and softmax confidence).  For i < M, with z_v the fp32 logit of row i
+ * (the accumulator of mosaic_masked_logits, before any bf16 rounding):
+ *   row_max[i]    = max_v z_v
+ *   row_argmax[i] = the smallest v with z_v == row_max[i]
+ *   row_lse[i]    = row_max[i] + log(sum_v exp(z_v - row_max[i]))   (fp32)
+ * softmax(z)_v = exp(z_v - row_lse[i]); the greedy token's confidence is
+ * exp(row_max[i] - row_lse[i]).
+ *   H, idx, W, M, chunk_rows   as for mosaic_masked_logits; in_dtype must be BF16 and
+ *                              d % 64 == 0 (else UNSUPPORTED).
+ *   out        NULL: the logits are never stored (no [M, V] buffer at all), or an
+ *              [M, V] row-major BF16 buffer (out_dtype BF16, else UNSUPPORTED) that
+ *              receives the same bits mosaic_masked_logits would write.
+ *   row_max    float[M], row_argmax int32[M], row_lse float[M]: device, 4-byte aligned.
+ *   workspace  device scratch of at least
+ *              mosaic_logits_argmax_lse_workspace_bytes(C, V) bytes, C = the rows of
+ *              the largest chunk (M when unchunked), 16-byte aligned; owned by the
+ *              caller; its contents on entry do not matter and on return are undefined.
+ * Results are deterministic and do not depend on chunk_rows.  M == 0: MOSAIC_OK and
+ * nothing is enqueued.  V == 0 with M > 0, a NULL required pointer, misalignment or a
+ * short workspace: INVALID_ARG; nothing is enqueued and no output is touched. */
+mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_t d,
+                                                const int32_t *idx, int64_t M,
+                                                const void *W, int64_t V,
+                                                void *out, int64_t chunk_rows,
+                                                mosaic_dtype_t in_dtype, mosaic_dtype_t out_dtype,
+                                                float *row_max, int32_t *row_argmax, float *row_lse,
+                                                void *workspace, int64_t workspace_bytes,
+                                                void *stream);
+
+/* Workspace bytes for launches of `rows` rows over V vocabulary entries:
+ * 12 * ceil(V / 256) * rows (three 4-byte partials per row and 256-entry tile), or -1
+ * on a negative size or int64 overflow. */
+int64_t mosaic_logits_argmax_lse_workspace_bytes(int64_t rows, int64_t V);
+
 /* ------------------------------------------------------------ host helpers --- */
 
 /* Number of chunks a call of mosaic_masked_logits makes for M rows ([DS] §3.2.2):

@@ -715,11 +715,21 @@ gather_gemm_bf16_persist_kernel(const __bf16 *__restrict__ H, const int32_t *__r
 //    all workgroups' results to memory while the matrix cores idle; spreading the stores
 //    over MFMA time removes most of that cost.  The last tile stores at once.
 // Same MFMA, operand roles and k order as the tiled kernel: results are bit-identical.
-template <int NSPREAD, int DEFER, int NIMM>
+//
+// REDUCE: the per-row consumer of the logits (largest logit, first index attaining it,
+// sum of exp(logit - largest)) is reduced from the fp32 accumulators of every tile
+// before they are rounded: each lane walks its 64 entries of a row in ascending
+// vocabulary order, the two lanes that share a row combine through permlane32_swap, and
+// the two waves that share the row's 256 entries combine through LDS.  One partial per
+// (row, vocabulary tile) goes to pmax / parg / psum ([nvt][rows], column-major so a
+// wave's 32 rows are consecutive words); mosaic_logits_reduce_finish combines them.
+// STORE = false skips the logits stores (consumer-only use: the logits never exist).
+template <int NSPREAD, int DEFER, int NIMM, bool STORE = true, bool REDUCE = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
 gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict__ idx, int32_t rows,
                               const __bf16 *__restrict__ W, int32_t V, int32_t d, __bf16 *__restrict__ out,
-                              int64_t ldo, int32_t group_m)
+                              int64_t ldo, int32_t group_m, float *__restrict__ pmax,
+                              int32_t *__restrict__ parg, float *__restrict__ psum)
 {
     constexpr int NW = 8, BV = 256, BM = 256, BK = 64, NSTAGE = 2;
     constexpr int ROW_BYTES = BK * 2;
@@ -741,6 +751,8 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     constexpr int SPS = (NST - NIMM) / DEFER; // deferred stores per K step
 
     __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+    // per-row partials of the upper vocabulary half (wv = 1) of a tile: [3][BM]
+    __shared__ float red_lds[REDUCE ? 3 * BM : 1];
 
     const int nvt = (V + BV - 1) / BV;
     const int nmt = (rows + BM - 1) / BM;
@@ -919,6 +931,90 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
             }
     };
 
+    // ---- per-row consumer partials of the current tile (REDUCE)
+    // (max, argmax, sum of exp(x - max)) pairs combine as: larger max wins, equal maxima
+    // keep the smaller index, sums are rescaled to the new max.  An empty partial is
+    // (-inf, INT32_MAX, 0).
+    constexpr float kLog2e = 1.4426950408889634f;
+    auto combine = [&](float &m, int &a, float &sm, float m2, int a2, float s2) {
+        const float mm = fmaxf(m, m2);
+        const bool take = m2 > m || (m2 == m && a2 < a);
+        const float e1 = (m == -INFINITY) ? 0.0f : sm * __builtin_amdgcn_exp2f((m - mm) * kLog2e);
+        const float e2 = (m2 == -INFINITY) ? 0.0f : s2 * __builtin_amdgcn_exp2f((m2 - mm) * kLog2e);
+        sm = e1 + e2;
+        a = take ? a2 : a;
+        m = mm;
+    };
+    float rm[AM], rs[AM];
+    int ra[AM];
+    // lane-pair partials of rows 32 * bm + fr of the wave's sub-tile; then the upper
+    // vocabulary half's waves leave theirs in LDS
+    auto reduce_part1 = [&](int v0) {
+#pragma unroll
+        for (int bm = 0; bm < AM; ++bm) {
+            float m = -INFINITY, sm = 0.0f;
+            int am = INT32_MAX;
+#pragma unroll
+            for (int a = 0; a < AV; ++a)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int v = v0 + wv * WV + a * 32 + gq * 8 + hi * 4 + j;
+                        const float x = acc[a][bm][gq * 4 + j];
+                        if (v < V && x > m) {
+                            m = x;
+                            am = v;
+                        }
+                    }
+#pragma unroll
+            for (int a = 0; a < AV; ++a)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int v = v0 + wv * WV + a * 32 + gq * 8 + hi * 4 + j;
+                        if (v < V)
+                            sm += __builtin_amdgcn_exp2f((acc[a][bm][gq * 4 + j] - m) * kLog2e);
+                    }
+            // the partner lane (same row, the other four entries of every group of 8)
+            const auto pm = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, m),
+                                                             __builtin_bit_cast(uint32_t, m), false, false);
+            const auto pa = __builtin_amdgcn_permlane32_swap((uint32_t)am, (uint32_t)am, false, false);
+            const auto ps = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, sm),
+                                                             __builtin_bit_cast(uint32_t, sm), false, false);
+            combine(m, am, sm, __builtin_bit_cast(float, hi ? pm[0] : pm[1]), (int)(hi ? pa[0] : pa[1]),
+                    __builtin_bit_cast(float, hi ? ps[0] : ps[1]));
+            rm[bm] = m;
+            ra[bm] = am;
+            rs[bm] = sm;
+            if (wv == 1 && hi == 0) {
+                const int r = wm * WM + bm * 32 + fr;
+                red_lds[r] = m;
+                red_lds[BM + r] = __builtin_bit_cast(float, am);
+                red_lds[2 * BM + r] = sm;
+            }
+        }
+    };
+    // after a barrier: the lower half's waves add the upper half and write the partial
+    auto reduce_part2 = [&](int m0, int v0) {
+        if (wv != 0 || hi != 0)
+            return;
+        const int64_t col = (int64_t)(v0 / BV) * rows;
+#pragma unroll
+        for (int bm = 0; bm < AM; ++bm) {
+            const int r = wm * WM + bm * 32 + fr;
+            float m = rm[bm], sm = rs[bm];
+            int am = ra[bm];
+            combine(m, am, sm, red_lds[r], __builtin_bit_cast(int, red_lds[BM + r]), red_lds[2 * BM + r]);
+            if (m0 + r < rows) {
+                pmax[col + m0 + r] = m;
+                parg[col + m0 + r] = am;
+                psum[col + m0 + r] = sm;
+            }
+        }
+    };
+
     bf16x8_t af[2][AV], bf[2][AM];
     const int npre = min(NSTAGE, nk);
     for (int s = 0; s < npre; ++s)
@@ -965,7 +1061,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
             rd = nx;
             ++kt;
         };
-        if (i > 0 && SPS > 0) {
+        if (STORE && i > 0 && SPS > 0) {
             if (nk >= NSTAGE + DEFER) {
 #pragma unroll
                 for (int j = 0; j < DEFER; ++j)
@@ -1000,6 +1096,10 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
             mma(af[(NSUB - 1) & 1], bf[(NSUB - 1) & 1]);
         }
         // every wave's last fragments are in registers: the stages are free
+        int cm0, cv0;
+        tile_coords(i, cm0, cv0);
+        if constexpr (REDUCE)
+            reduce_part1(cv0);
         wait_vmcnt<63>();
         barrier_no_fence();
         if (i + 1 < n_my) {
@@ -1009,17 +1109,93 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
                 for (int p = 0; p < NSPREAD; ++p)
                     issue_part(s * STAGE, s, p);
         }
-        tile_coords(i, pm0, pv0);
-        pack();
+        if constexpr (REDUCE)
+            reduce_part2(cm0, cv0);
+        if constexpr (STORE) {
+            pm0 = cm0;
+            pv0 = cv0;
+            pack();
 #pragma unroll
-        for (int j = 0; j < NIMM; ++j)
-            store_one(j);
-        if (i + 1 == n_my) {
-#pragma unroll
-            for (int j = NIMM; j < NST; ++j)
+            for (int j = 0; j < NIMM; ++j)
                 store_one(j);
+            if (i + 1 == n_my) {
+#pragma unroll
+                for (int j = NIMM; j < NST; ++j)
+                    store_one(j);
+            }
+        } else {
+#pragma unroll
+            for (int a = 0; a < AV; ++a)
+#pragma unroll
+                for (int bm = 0; bm < AM; ++bm)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        acc[a][bm][e] = 0.0f;
         }
         load_hidx(i + 2);
+        if constexpr (REDUCE) {
+            // red_lds is rewritten at the next tile's end; its readers finish first
+            // (that tile's K loop has barriers), so no extra barrier is needed here.
+        }
+    }
+}
+
+// Combine the per-(row, vocabulary tile) partials of the REDUCE kernel into the per-row
+// consumer outputs: row_max, row_argmax (the first index attaining the max) and
+// row_lse = max + log(sum_v exp(z_v - max)).  A workgroup owns 64 rows; its eight waves
+// take eight contiguous ranges of tiles (max pass, then sum pass) and are combined in
+// range order through LDS, so the result does not depend on timing or on how the rows
+// were chunked.
+__global__ __launch_bounds__(512) void logits_reduce_finish_kernel(const float *__restrict__ pmax,
+                                                                  const int32_t *__restrict__ parg,
+                                                                  const float *__restrict__ psum, int32_t ncol,
+                                                                  int32_t rows, float *__restrict__ row_max,
+                                                                  int32_t *__restrict__ row_argmax,
+                                                                  float *__restrict__ row_lse)
+{
+    constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+    __shared__ float sm_m[8][64], sm_s[8][64];
+    __shared__ int32_t sm_a[8][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r = blockIdx.x * 64 + lane;
+    const int c0 = (int)((int64_t)ncol * w / 8), c1 = (int)((int64_t)ncol * (w + 1) / 8);
+    float m = -INFINITY, s = 0.0f;
+    int a = INT32_MAX;
+    if (r < rows) {
+        for (int c = c0; c < c1; ++c) {
+            const float x = pmax[(int64_t)c * rows + r];
+            const int ax = parg[(int64_t)c * rows + r];
+            if (x > m || (x == m && ax < a)) {
+                m = x;
+                a = ax;
+            }
+        }
+        if (m != -INFINITY)
+            for (int c = c0; c < c1; ++c) {
+                const float x = pmax[(int64_t)c * rows + r];
+                if (x != -INFINITY)
+                    s += psum[(int64_t)c * rows + r] * __builtin_amdgcn_exp2f((x - m) * kLog2e);
+            }
+    }
+    sm_m[w][lane] = m;
+    sm_a[w][lane] = a;
+    sm_s[w][lane] = s;
+    __syncthreads();
+    if (w == 0 && r < rows) {
+        float mm = -INFINITY;
+        int aa = INT32_MAX;
+        for (int k = 0; k < 8; ++k)
+            if (sm_m[k][lane] > mm || (sm_m[k][lane] == mm && sm_a[k][lane] < aa)) {
+                mm = sm_m[k][lane];
+                aa = sm_a[k][lane];
+            }
+        float ss = 0.0f;
+        for (int k = 0; k < 8; ++k)
+            if (sm_m[k][lane] != -INFINITY)
+                ss += sm_s[k][lane] * __builtin_amdgcn_exp2f((sm_m[k][lane] - mm) * kLog2e);
+        row_max[r] = mm;
+        row_argmax[r] = aa;
+        row_lse[r] = mm + __builtin_amdgcn_logf(ss) * kLn2;
     }
 }
 
@@ -1348,9 +1524,10 @@ hipError_t launch_persist(const void *H, const int32_t *idx, int64_t rows, const
     return hipGetLastError();
 }
 
-template <int NSPREAD, int DEFER, int NIMM>
+template <int NSPREAD, int DEFER, int NIMM, bool STORE = true, bool REDUCE = false>
 hipError_t launch_defer(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V, int64_t d,
-                        void *out, int64_t ldo, int group_m, hipStream_t stream)
+                        void *out, int64_t ldo, int group_m, hipStream_t stream, float *pmax = nullptr,
+                        int32_t *parg = nullptr, float *psum = nullptr)
 {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
@@ -1358,9 +1535,9 @@ hipError_t launch_defer(const void *H, const int32_t *idx, int64_t rows, const v
     const int64_t ntiles = ((V + 255) / 256) * ((rows + 255) / 256);
     int64_t grid = std::max<int64_t>(8, (cus / 8) * 8);
     grid = std::min<int64_t>(grid, ((ntiles + 7) / 8) * 8);
-    hipLaunchKernelGGL((gather_gemm_bf16_defer_kernel<NSPREAD, DEFER, NIMM>), dim3((unsigned)grid), dim3(512), 0,
-                       stream, (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d,
-                       (__bf16 *)out, ldo, group_m);
+    hipLaunchKernelGGL((gather_gemm_bf16_defer_kernel<NSPREAD, DEFER, NIMM, STORE, REDUCE>), dim3((unsigned)grid),
+                       dim3(512), 0, stream, (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V,
+                       (int32_t)d, (__bf16 *)out, ldo, group_m, pmax, parg, psum);
     return hipGetLastError();
 }
 
@@ -1412,6 +1589,25 @@ bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V)
     default:
         return false;
     }
+}
+
+hipError_t launch_logits_argmax_lse(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V,
+                                    int64_t d, void *out, int64_t ldo, float *pmax, int32_t *parg, float *psum,
+                                    float *row_max, int32_t *row_argmax, float *row_lse, int group_m,
+                                    hipStream_t stream)
+{
+    if (group_m <= 0)
+        group_m = kDefaultGroupM;
+    const hipError_t e =
+        out ? launch_defer<2, 4, 8, true, true>(H, idx, rows, W, V, d, out, ldo, group_m, stream, pmax, parg, psum)
+            : launch_defer<2, 4, 8, false, true>(H, idx, rows, W, V, d, nullptr, ldo, group_m, stream, pmax, parg,
+                                                 psum);
+    if (e != hipSuccess)
+        return e;
+    const int ncol = (int)((V + 255) / 256);
+    hipLaunchKernelGGL(logits_reduce_finish_kernel, dim3((unsigned)((rows + 63) / 64)), dim3(512), 0, stream, pmax,
+                       parg, psum, ncol, (int32_t)rows, row_max, row_argmax, row_lse);
+    return hipGetLastError();
 }
 
 hipError_t launch_gather_gemm(int variant, const void *H, const int32_t *idx, int64_t rows, const void *W,

@@ -48,4 +48,13 @@ hipError_t launch_gather_gemm(int variant, const void *H, const int32_t *idx, in
                               const void *W, int64_t V, int64_t d, void *out, int64_t ldo,
                               bool out_bf16, int group_m, hipStream_t stream);
 
+// One chunk of the per-row consumer (bf16 in, d % 64 == 0): the persistent kernel
+// reduces every (row, 256-entry vocabulary tile) to a partial in pmax / parg / psum
+// ([ceil(V/256)][rows] each) and, when `out` is not null, also stores the bf16 logits;
+// a finish kernel combines the partials into row_max / row_argmax / row_lse.
+hipError_t launch_logits_argmax_lse(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V,
+                                    int64_t d, void *out, int64_t ldo, float *pmax, int32_t *parg, float *psum,
+                                    float *row_max, int32_t *row_argmax, float *row_lse, int group_m,
+                                    hipStream_t stream);
+
 }  // namespace mosaic

@@ -238,4 +238,67 @@ mosaic_status_t mosaic_masked_logits(const void *H, int64_t L, int64_t d, const 
     return MOSAIC_OK;
 }
 
+int64_t mosaic_logits_argmax_lse_workspace_bytes(int64_t rows, int64_t V)
+{
+    if (rows < 0 || V < 0)
+        return -1;
+    const int64_t ncol = (V + 255) / 256;
+    const int64_t n = checked_bytes(ncol, rows, 12);
+    return n < 0 ? -1 : n;
+}
+
+mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_t d, const int32_t *idx, int64_t M,
+                                                const void *W, int64_t V, void *out, int64_t chunk_rows,
+                                                mosaic_dtype_t in_dtype, mosaic_dtype_t out_dtype, float *row_max,
+                                                int32_t *row_argmax, float *row_lse, void *workspace,
+                                                int64_t workspace_bytes, void *stream)
+{
+    if (M < 0 || V < 0 || L < 0 || d < 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (esize_of(in_dtype) == 0 || (out && esize_of(out_dtype) == 0))
+        return MOSAIC_ERR_INVALID_ARG;
+    if (M == 0)
+        return MOSAIC_OK;   // no rows: nothing to compute
+    if (V == 0)
+        return MOSAIC_ERR_INVALID_ARG;   // the maximum of an empty row does not exist
+    if (in_dtype != MOSAIC_BF16 || (out && out_dtype != MOSAIC_BF16))
+        return MOSAIC_ERR_UNSUPPORTED;
+    if (d % 64 != 0 || d > (1 << 22))
+        return MOSAIC_ERR_UNSUPPORTED;
+    if (!H || !W || !idx || !row_max || !row_argmax || !row_lse || !workspace || L == 0 || d == 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (!aligned16(H) || !aligned16(W) || (out && !aligned16(out)) || !aligned16(workspace) ||
+        ((uintptr_t)idx & 3u) || ((uintptr_t)row_max & 3u) || ((uintptr_t)row_argmax & 3u) ||
+        ((uintptr_t)row_lse & 3u))
+        return MOSAIC_ERR_INVALID_ARG;
+    if ((out && checked_bytes(M, V, 2) < 0) || checked_bytes(L, d, 2) < 0 || checked_bytes(V, d, 2) < 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (L > kMaxPos || V > kMaxPos || d > kMaxPos)
+        return MOSAIC_ERR_UNSUPPORTED;
+    const int64_t K = mosaic_num_chunks(M, chunk_rows);
+    const int64_t C = (K == 1) ? M : chunk_rows;
+    if (C > kMaxPos || !mosaic::gather_gemm_grid_fits(mosaic::kVariantBf16DeferS4I8, C, V))
+        return MOSAIC_ERR_UNSUPPORTED;
+    const int64_t need = mosaic_logits_argmax_lse_workspace_bytes(C, V);
+    if (need < 0 || workspace_bytes < need)
+        return MOSAIC_ERR_INVALID_ARG;
+    // workspace: pmax, parg, psum, each [ceil(V/256)][C] 4-byte words
+    const int64_t plane = (V + 255) / 256 * C;
+    float *pmax = (float *)workspace;
+    int32_t *parg = (int32_t *)(pmax + plane);
+    float *psum = (float *)(parg + plane);
+    const int group_m = read_tune().group_m;
+    for (int64_t k = 0; k < K; ++k) {
+        const int64_t r0 = k * C;
+        const int64_t r1 = (r0 + C < M) ? r0 + C : M;
+        void *chunk_out = out ? (char *)out + r0 * V * 2 : nullptr;
+        const hipError_t e = mosaic::launch_logits_argmax_lse(H, idx + r0, r1 - r0, W, V, d, chunk_out, V, pmax,
+                                                              parg, psum, row_max + r0, row_argmax + r0,
+                                                              row_lse + r0, group_m, (hipStream_t)stream);
+        if (e != hipSuccess)
+            return MOSAIC_ERR_DEVICE;
+    }
+    return MOSAIC_OK;
+}
+
 }  // extern "C"

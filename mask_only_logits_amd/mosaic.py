@@ -34,6 +34,8 @@ EXPORTS = (
     "mosaic_num_chunks",
     "mosaic_logits_bytes",
     "mosaic_logits_variant",
+    "mosaic_masked_logits_argmax_lse",
+    "mosaic_logits_argmax_lse_workspace_bytes",
 )
 
 
@@ -65,6 +67,10 @@ def _load() -> ctypes.CDLL:
     lib.mosaic_logits_bytes.argtypes = [i64, i64, st, ctypes.POINTER(i64)]
     lib.mosaic_logits_variant.restype = ctypes.c_int
     lib.mosaic_logits_variant.argtypes = [i64, i64, i64, st, st]
+    lib.mosaic_masked_logits_argmax_lse.restype = st
+    lib.mosaic_masked_logits_argmax_lse.argtypes = [p, i64, i64, p, i64, p, i64, p, i64, st, st, p, p, p, p, i64, p]
+    lib.mosaic_logits_argmax_lse_workspace_bytes.restype = i64
+    lib.mosaic_logits_argmax_lse_workspace_bytes.argtypes = [i64, i64]
     return lib
 
 
@@ -201,3 +207,56 @@ def mosaic_masked_logits(H: torch.Tensor, idx: torch.Tensor, W: torch.Tensor, M:
                                     _dev(out, "out"), int(chunk_rows), _dtype_code(H.dtype),
                                     _dtype_code(out.dtype), _stream(stream)), "mosaic_masked_logits")
     return out
+
+
+def mosaic_logits_argmax_lse_workspace_bytes(rows: int, V: int) -> int:
+    """Workspace bytes mosaic_masked_logits_argmax_lse needs for launches of `rows` rows."""
+    n = int(lib.mosaic_logits_argmax_lse_workspace_bytes(int(rows), int(V)))
+    if n < 0:
+        raise ValueError("workspace size overflows")
+    return n
+
+
+def mosaic_masked_logits_argmax_lse(H: torch.Tensor, idx: torch.Tensor, W: torch.Tensor, M: int | None = None,
+                                    chunk_rows: int = 0, store_logits: bool = False,
+                                    out: torch.Tensor | None = None, row_max: torch.Tensor | None = None,
+                                    row_argmax: torch.Tensor | None = None, row_lse: torch.Tensor | None = None,
+                                    workspace: torch.Tensor | None = None, stream=None):
+    """Per masked row i: (row_max[i], row_argmax[i], row_lse[i]) of its fp32 logits
+    H[idx[i]] . W^T -- the largest logit, the first vocabulary index attaining it and
+    log(sum_v exp(logit_v)).  bf16 H [L, d] and W [V, d] with d % 64 == 0.
+
+    The logits are stored only if `store_logits` (or `out` is given): then `out`
+    ([M, V] bf16, allocated if absent) holds them and is returned as the fourth item,
+    else the fourth item is None.  `workspace` (uint8, allocated if absent) must hold
+    mosaic_logits_argmax_lse_workspace_bytes(min(M, chunk_rows or M), V) bytes."""
+    if H.dim() != 2 or W.dim() != 2 or H.shape[1] != W.shape[1]:
+        raise ValueError("H must be [L, d] and W [V, d]")
+    L, d = H.shape
+    V = W.shape[0]
+    M = idx.numel() if M is None else int(M)
+    if M > idx.numel():
+        raise ValueError("M exceeds the length of idx")
+    dev = H.device
+    if store_logits and out is None:
+        out = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
+    if out is not None and out.numel() < M * V:
+        raise ValueError("out is smaller than M * V")
+    row_max = torch.empty(M, dtype=torch.float32, device=dev) if row_max is None else row_max
+    row_argmax = torch.empty(M, dtype=torch.int32, device=dev) if row_argmax is None else row_argmax
+    row_lse = torch.empty(M, dtype=torch.float32, device=dev) if row_lse is None else row_lse
+    for name, t in (("row_max", row_max), ("row_argmax", row_argmax), ("row_lse", row_lse)):
+        if t.numel() < M:
+            raise ValueError(f"{name} has fewer than M entries")
+    C = M if chunk_rows <= 0 or chunk_rows >= M else int(chunk_rows)
+    need = mosaic_logits_argmax_lse_workspace_bytes(C, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(lib.mosaic_masked_logits_argmax_lse(
+        _dev(H, "H"), L, d, _dev(idx, "idx", torch.int32), M, _dev(W, "W"), V,
+        _dev(out, "out") if out is not None else None, int(chunk_rows), _dtype_code(H.dtype),
+        _dtype_code(out.dtype) if out is not None else MOSAIC_BF16,
+        _dev(row_max, "row_max", torch.float32), _dev(row_argmax, "row_argmax", torch.int32),
+        _dev(row_lse, "row_lse", torch.float32), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(stream)), "mosaic_masked_logits_argmax_lse")
+    return row_max, row_argmax, row_lse, out

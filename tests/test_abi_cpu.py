@@ -128,3 +128,41 @@ def test_product_path_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in text and "liboracle" not in text, f
+
+
+def _argmax_lse(m, H=A16, L=100, d=64, idx=A16, M=10, W=A16, V=50, out=None, C=0, i=1, o=1,
+                rmax=A16, rarg=A16, rlse=A16, ws=A16, wsb=1 << 20):
+    return m.lib.mosaic_masked_logits_argmax_lse(H, L, d, idx, M, W, V, out, C, i, o, rmax, rarg, rlse, ws, wsb,
+                                                 None)
+
+
+def test_argmax_lse_workspace_bytes(m):
+    f = m.lib.mosaic_logits_argmax_lse_workspace_bytes
+    assert f(4096, 126464) == 12 * 494 * 4096
+    assert f(10, 1) == 120 and f(10, 256) == 120 and f(10, 257) == 240
+    assert f(0, 100) == 0
+    assert f(-1, 10) == -1 and f(10, -1) == -1
+    assert f(2**62, 2**20) == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), 1), (dict(V=-1), 1), (dict(L=-1), 1), (dict(d=-1), 1),
+    (dict(V=0), 1),                                     # the max of an empty row does not exist
+    (dict(i=0), 2), (dict(i=0, d=4), 2),                # fp32 inputs are not offered
+    (dict(d=72), 2), (dict(d=96), 2),                   # needs d % 64 == 0
+    (dict(out=A16, o=0), 2),                            # stored logits are bf16 only
+    (dict(i=7), 1), (dict(out=A16, o=7), 1),
+    (dict(H=None), 1), (dict(W=None), 1), (dict(idx=None), 1),
+    (dict(rmax=None), 1), (dict(rarg=None), 1), (dict(rlse=None), 1), (dict(ws=None), 1),
+    (dict(H=A8), 1), (dict(ws=A8), 1), (dict(out=A8), 1), (dict(rmax=A16 + 2), 1), (dict(idx=A16 + 1), 1),
+    (dict(wsb=12 * 1 * 10 - 1), 1),                     # one 256-entry tile x 10 rows needs 120 bytes
+    (dict(V=300, wsb=12 * 1 * 10), 1),                  # two tiles need 240
+    (dict(M=1000, C=100, wsb=12 * 1 * 100 - 4), 1),     # sized by the chunk, not by M
+    (dict(L=2**31), 2),
+])
+def test_argmax_lse_validation(m, kw, status):
+    assert _argmax_lse(m, **kw) == status
+
+
+def test_argmax_lse_empty_is_ok_without_pointers(m):
+    assert _argmax_lse(m, M=0, H=None, W=None, idx=None, rmax=None, rarg=None, rlse=None, ws=None, wsb=0) == 0
