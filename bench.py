@@ -46,10 +46,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def _profile_tag(workload: str, path: str) -> str:
+    return workload if path == "logits" else f"{workload}_{path}"
+
+
+def measured_traffic(workload: str, path: str = "logits"):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_gather_gemm_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_gather_gemm_{_profile_tag(workload, path)}.json")
     try:
         with open(path, encoding="utf-8") as fh:
             t = json.load(fh)
@@ -60,22 +64,24 @@ def measured_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, idx_np, target_s: float):
+def cpu_baseline(wl, idx_np, target_s: float, path: str = "logits"):
     """Time the oracle on a bounded sample of masked rows (the first rows of idx)."""
     import oracle
     cores = oracle.num_threads()
     flop_row = 2.0 * wl.d * wl.V
+    fn = oracle.masked_logits if path == "logits" else oracle.masked_logits_argmax_lse
     t0 = time.perf_counter()
-    oracle.masked_logits(wl.H, idx_np, wl.W, rows=list(range(2)))
+    fn(wl.H, idx_np, wl.W, rows=list(range(2)))
     t_cal = max(1e-3, time.perf_counter() - t0) / 2
     n = int(max(2, min(len(idx_np), target_s / t_cal)))
     rows = list(range(n))
     t0 = time.perf_counter()
-    oracle.masked_logits(wl.H, idx_np, wl.W, rows=rows)
+    fn(wl.H, idx_np, wl.W, rows=rows)
     dt = time.perf_counter() - t0
     return {"value": round(n * flop_row / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} of {len(idx_np)} masked rows x all {wl.V} vocabulary rows of the same workload "
-                      f"(fp64, ascending k), {dt:.1f} s"}
+                      f"(fp64, ascending k{'' if path == 'logits' else ', then max / argmax / log-sum-exp'}), "
+                      f"{dt:.1f} s"}
 
 
 def _read_csv(path):
@@ -91,7 +97,7 @@ def _find(root, suffix):
     return sorted(out)
 
 
-def summarize_profile(root: str, workload: str, copy_mib: int):
+def summarize_profile(root: str, workload: str, copy_mib: int, path: str = "logits"):
     """Write profiles/ summaries from rocprofv3 output under `root`: kernel_stats
     (--kernel-trace --stats) and counter_collection (--pmc) CSV files.  `root/commands.txt`,
     if present, holds the rocprofv3 command lines that produced them; it is copied in."""
@@ -99,7 +105,9 @@ def summarize_profile(root: str, workload: str, copy_mib: int):
     os.makedirs(prof, exist_ok=True)
     stats = _find(root, "kernel_stats.csv")
     counters = _find(root, "counter_collection.csv")
-    lines = [f"# rocprofv3 summary: gather-GEMM on workload {workload}", ""]
+    tag = _profile_tag(workload, path)
+    lines = [f"# rocprofv3 summary: gather-GEMM on workload {workload}"
+             + ("" if path == "logits" else f" ({path} path: logits reduced per row, not stored)"), ""]
     cmd_file = os.path.join(root, "commands.txt")
     if os.path.exists(cmd_file):
         lines += ["Commands (run from the repository root):", "```"]
@@ -141,15 +149,15 @@ def summarize_profile(root: str, workload: str, copy_mib: int):
         w_scale = known / (sum(cp["WRITE_SIZE"]) / len(cp["WRITE_SIZE"]) * 1024)
         fetch = sum(g["FETCH_SIZE"]) / len(g["FETCH_SIZE"]) * 1024 * f_scale
         write = sum(g["WRITE_SIZE"]) / len(g["WRITE_SIZE"]) * 1024 * w_scale
-        traffic = {"kernel_source_hash": kernel_source_hash(), "workload": workload,
+        traffic = {"kernel_source_hash": kernel_source_hash(), "workload": workload, "path": path,
                    "bytes_per_launch": int(fetch + write), "fetch_bytes_per_launch": int(fetch),
                    "write_bytes_per_launch": int(write), "fetch_scale": f_scale, "write_scale": w_scale,
                    "copy_probe_bytes": known}
-        with open(os.path.join(prof, f"traffic_gather_gemm_{workload}.json"), "w", encoding="utf-8") as fh:
+        with open(os.path.join(prof, f"traffic_gather_gemm_{tag}.json"), "w", encoding="utf-8") as fh:
             json.dump(traffic, fh, indent=1)
         lines.append(f"traffic per GEMM launch (scaled by the copy probe): fetch {fetch / 1e9:.3f} GB, "
                      f"write {write / 1e9:.3f} GB (scales {f_scale:.4f}, {w_scale:.4f})")
-    out = os.path.join(prof, f"gather_gemm_{workload}_rocprof.md")
+    out = os.path.join(prof, f"gather_gemm_{tag}_rocprof.md")
     with open(out, "w", encoding="utf-8") as fh:
         fh.write("\n".join(lines) + "\n")
     log(f"[bench] wrote {out}")
@@ -168,10 +176,13 @@ def main():
                          "(a kernel of known traffic that calibrates rocprofv3's FETCH_SIZE/WRITE_SIZE)")
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="summarize rocprofv3 CSV output found under DIR into profiles/ and exit")
+    ap.add_argument("--path", choices=("logits", "argmax_lse"), default="logits",
+                    help="logits: store the bf16 logits of every masked row (default); argmax_lse: reduce each "
+                         "row to (max, first argmax, log-sum-exp) inside the kernel and store no logits")
     args = ap.parse_args()
 
     if args.summarize_profile:
-        summarize_profile(args.summarize_profile, args.workload, args.profile_copy_mib or 1024)
+        summarize_profile(args.summarize_profile, args.workload, args.profile_copy_mib or 1024, args.path)
         return
 
     if args.gpus != 1:
@@ -207,13 +218,29 @@ def main():
     else:
         mosaic.mosaic_mask_compact(tokens, wl.mask_id, idx=idx, count=cnt[:1])
         M = int(cnt[0].item())
-    out = torch.empty((M, V), dtype=out_dtype, device=dev)
     C = wl.chunk_rows
     launches = mosaic.mosaic_num_chunks(M, C)
     flop = 2.0 * M * d * V
     rows_per_launch = M if launches == 1 else C
-    variant = mosaic.mosaic_logits_variant(rows_per_launch, V, d, H.dtype, out_dtype)
-    log(f"[bench] M={M} chunk_rows={C} launches={launches} variant={variant} out={out.numel() * out.element_size() / 1e9:.2f} GB")
+    consumer = args.path == "argmax_lse"
+    if consumer:
+        if wl.dtype != "bf16" or d % 64:
+            log(f"[bench] the argmax_lse path needs bf16 inputs and d % 64 == 0 ({args.workload} has not)")
+            sys.exit(2)
+        out = None
+        rmax = torch.empty(M, dtype=torch.float32, device=dev)
+        rarg = torch.empty(M, dtype=torch.int32, device=dev)
+        rlse = torch.empty(M, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(16, mosaic.mosaic_logits_argmax_lse_workspace_bytes(rows_per_launch, V)),
+                         dtype=torch.uint8, device=dev)
+        variant = None
+        log(f"[bench] M={M} chunk_rows={C} launches={launches} path=argmax_lse (no logits stored) "
+            f"workspace={ws.numel() / 1e6:.1f} MB")
+    else:
+        out = torch.empty((M, V), dtype=out_dtype, device=dev)
+        variant = mosaic.mosaic_logits_variant(rows_per_launch, V, d, H.dtype, out_dtype)
+        log(f"[bench] M={M} chunk_rows={C} launches={launches} variant={variant} "
+            f"out={out.numel() * out.element_size() / 1e9:.2f} GB")
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -230,7 +257,11 @@ def main():
             m = int(cnt[0].item())
         if i is not None:
             ev[i][1].record(stream)
-        mosaic.mosaic_masked_logits(H, idx, W, M=m, out=out, chunk_rows=C, stream=stream)
+        if consumer:
+            mosaic.mosaic_masked_logits_argmax_lse(H, idx, W, M=m, chunk_rows=C, row_max=rmax, row_argmax=rarg,
+                                                   row_lse=rlse, workspace=ws, stream=stream)
+        else:
+            mosaic.mosaic_masked_logits(H, idx, W, M=m, out=out, chunk_rows=C, stream=stream)
         if i is not None:
             ev[i][2].record(stream)
         return m
@@ -254,9 +285,10 @@ def main():
         f"{gemm_avg / launches:.3f} ms per launch; compaction+readback {np.mean(compact_ms) * 1e3:.1f} us")
 
     esize_in = 2 if wl.dtype == "bf16" else 4
-    alg_bytes = launches * V * d * esize_in + M * d * esize_in + M * V * out.element_size() + M * 4
-    traffic = measured_traffic(args.workload)
-    kernel = {0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel", 6: "gather_gemm_lowm_kernel",
+    out_bytes = M * 12 if consumer else M * V * out.element_size()
+    alg_bytes = launches * V * d * esize_in + M * d * esize_in + out_bytes + M * 4
+    traffic = measured_traffic(args.workload, args.path)
+    kernel = "gather_gemm_bf16_defer_kernel" if consumer else {0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel", 6: "gather_gemm_lowm_kernel",
               9: "gather_gemm_bf16_persist_kernel", 10: "gather_gemm_bf16_persist_kernel",
               11: "gather_gemm_bf16_persist_kernel", 15: "gather_gemm_bf16_defer_kernel",
               16: "gather_gemm_bf16_defer_kernel", 17: "gather_gemm_bf16_defer_kernel"}.get(variant, "gather_gemm_bf16_kernel")
@@ -285,8 +317,9 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded Gaussian H ~ N(0,1), W ~ N(0,0.02); uniform masked positions)",
         "config": {"workload": args.workload, "L": L, "d": d, "V": V, "M": M, "chunk_rows": C,
-                   "launches_per_step": launches, "in_dtype": wl.dtype, "out_dtype": wl.out_dtype,
-                   "accumulate": "fp32"},
+                   "launches_per_step": launches, "in_dtype": wl.dtype,
+                   "out_dtype": "per-row f32 max / i32 argmax / f32 lse" if consumer else wl.out_dtype,
+                   "accumulate": "fp32", "path": args.path},
         "roofline": roofline,
         "detail": {"gemm_ms_per_step": round(gemm_avg, 4), "gemm_ms_min": round(min(gemm_ms), 4),
                    "compaction_readback_us": round(float(np.mean(compact_ms)) * 1e3, 2)},
@@ -304,7 +337,7 @@ def main():
     if not args.no_cpu_baseline:
         idx_np = idx[:M].cpu().numpy()
         log("[bench] timing the CPU oracle on a row sample ...")
-        result["cpu_baseline"] = cpu_baseline(wl, idx_np, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, idx_np, args.cpu_seconds, args.path)
         log(f"[bench] cpu_baseline {result['cpu_baseline']}")
     else:
         result["cpu_baseline"] = None

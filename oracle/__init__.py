@@ -65,6 +65,8 @@ def _load():
         lib.oracle_masked_logits_argmax_lse_bf16.restype = ctypes.c_int
         lib.oracle_masked_logits_argmax_lse_bf16.argtypes = [_p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
                                                              _p, _p, _p]
+        lib.oracle_lazy_chunk_rows.restype = ctypes.c_int
+        lib.oracle_lazy_chunk_rows.argtypes = [_i64, _i64, _i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
         lib.oracle_logits_bytes.restype = _i64
         lib.oracle_logits_bytes.argtypes = [_i64, _i64, _i64]
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -138,6 +140,16 @@ def chunk_range(M: int, C: int, k: int):
     r0, r1 = _i64(), _i64()
     _load().oracle_chunk_range(int(M), int(C), int(k), ctypes.byref(r0), ctypes.byref(r1))
     return int(r0.value), int(r1.value)
+
+
+def lazy_chunk_rows(M: int, V: int, esize: int, budget: int):
+    """(chunk_rows, num_chunks) of the lazy chunk choice; chunk_rows 0 = no chunking.
+    Raises ValueError when one row does not fit the budget."""
+    c, k = _i64(), _i64()
+    rc = _load().oracle_lazy_chunk_rows(int(M), int(V), int(esize), int(budget), ctypes.byref(c), ctypes.byref(k))
+    if rc != 0:
+        raise ValueError("one row of logits does not fit the budget")
+    return int(c.value), int(k.value)
 
 
 def masked_logits(H, idx, W, rows=None) -> np.ndarray:

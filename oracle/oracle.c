@@ -28,6 +28,13 @@
  *      or two fp32 values are exact in fp64).  No bias, scale or softcap: the pages
  *      name only the lm_head projection.
  *
+ *  (2b) lazy chunk choice -- Mosaic's lazy chunking applied to the logits operator
+ *      ("扩散大语言模型内存优化：Mosaic系统突破与实践", §2.3; Mosaic review, 核心组件 3):
+ *      chunking is off unless the memory available for the logits is too small, and
+ *      then the smallest number of chunks that fits is used.  The oracle searches k =
+ *      1, 2, ... and stops at the first k whose largest chunk, ceil(M / k) rows, fits
+ *      the byte budget; the chunks are then ceil(M / k) rows each (the last shorter).
+ *
  *  (4) per-row consumer -- what the sampler reads from a masked row's logits z[v]:
  *      the largest logit, the first vocabulary index that attains it (greedy
  *      decoding), and log(sum_v exp z[v]), from which the softmax confidence of any
@@ -108,6 +115,33 @@ void oracle_chunk_range(int64_t M, int64_t C, int64_t k, int64_t *r0, int64_t *r
     }
     *r0 = k * C;
     *r1 = (k + 1) * C < M ? (k + 1) * C : M;
+}
+
+/* (2b) Lazy chunk choice for M rows of V entries of esize bytes under a budget of
+ * `budget` bytes for the logits buffer.  Sets *chunk_rows (0 = no chunking) and
+ * *num_chunks.  Returns 0, or -1 when one row does not fit (V * esize > budget) or an
+ * argument is negative. */
+int oracle_lazy_chunk_rows(int64_t M, int64_t V, int64_t esize, int64_t budget, int64_t *chunk_rows,
+                           int64_t *num_chunks)
+{
+    if (M < 0 || V < 0 || esize <= 0 || budget < 0)
+        return -1;
+    if (M == 0) {
+        *chunk_rows = 0;
+        *num_chunks = 0;
+        return 0;
+    }
+    for (int64_t k = 1; k <= M; ++k) {
+        const int64_t rows = (M + k - 1) / k;            /* the largest chunk */
+        /* rows * V * esize <= budget, without overflow */
+        const int fits = V == 0 || (rows <= budget / esize / V && rows * V * esize <= budget);
+        if (fits) {
+            *chunk_rows = (k == 1) ? 0 : rows;
+            *num_chunks = k;
+            return 0;
+        }
+    }
+    return -1;
 }
 
 /* ------------------------------------------------------------------ (3) logits */
