@@ -173,6 +173,17 @@ int64_t mosaic_logits_argmax_lse_workspace_bytes(int64_t rows, int64_t V);
  * 0 for M <= 0, 1 for chunk_rows <= 0 or chunk_rows >= M, else ceil(M / chunk_rows). */
 int64_t mosaic_num_chunks(int64_t M, int64_t chunk_rows);
 
+/* Lazy chunk choice for the logits operator ([MP] §2.3; [MR] 核心组件 3): chunking is
+ * off while the whole [M, V] buffer of out_dtype fits budget_bytes (*chunk_rows = 0,
+ * *num_chunks = 1); otherwise *num_chunks = k, the smallest k whose largest chunk,
+ * ceil(M / k) rows, fits, and *chunk_rows = ceil(M / k), so that passing it to
+ * mosaic_masked_logits makes exactly k balanced chunks.  M == 0 gives (0, 0).
+ * UNSUPPORTED when one row does not fit (V * esize > budget_bytes); INVALID_ARG on a
+ * negative size, an unknown dtype or a NULL output pointer. */
+mosaic_status_t mosaic_lazy_chunk_rows(int64_t M, int64_t V, mosaic_dtype_t out_dtype,
+                                      int64_t budget_bytes, int64_t *chunk_rows,
+                                      int64_t *num_chunks);
+
 /* Bytes of a logits tensor of `rows` rows over V vocabulary entries of dtype `dt`
  * ([DS] §2.2): rows * V * esize, written to *bytes.  INVALID_ARG on a negative size,
  * an unknown dtype, a NULL `bytes` or overflow of int64. */

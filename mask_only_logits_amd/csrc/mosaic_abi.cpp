@@ -238,6 +238,34 @@ mosaic_status_t mosaic_masked_logits(const void *H, int64_t L, int64_t d, const 
     return MOSAIC_OK;
 }
 
+mosaic_status_t mosaic_lazy_chunk_rows(int64_t M, int64_t V, mosaic_dtype_t out_dtype, int64_t budget_bytes,
+                                      int64_t *chunk_rows, int64_t *num_chunks)
+{
+    const int64_t es = esize_of(out_dtype);
+    if (M < 0 || V < 0 || budget_bytes < 0 || es == 0 || !chunk_rows || !num_chunks)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (M == 0) {
+        *chunk_rows = 0;
+        *num_chunks = 0;
+        return MOSAIC_OK;
+    }
+    const int64_t all = checked_bytes(M, V, es);
+    if (all >= 0 && all <= budget_bytes) {   // the whole buffer fits: chunking stays off
+        *chunk_rows = 0;
+        *num_chunks = 1;
+        return MOSAIC_OK;
+    }
+    // rows that fit: r = floor(budget / (V * es)); the fewest chunks is ceil(M / r), and
+    // balanced chunks of ceil(M / k) rows (<= r) give exactly k chunks in the driver
+    const int64_t r = budget_bytes / es / V;
+    if (r < 1)
+        return MOSAIC_ERR_UNSUPPORTED;
+    const int64_t k = (M + r - 1) / r;
+    *chunk_rows = (M + k - 1) / k;
+    *num_chunks = k;
+    return MOSAIC_OK;
+}
+
 int64_t mosaic_logits_argmax_lse_workspace_bytes(int64_t rows, int64_t V)
 {
     if (rows < 0 || V < 0)

@@ -36,6 +36,7 @@ EXPORTS = (
     "mosaic_logits_variant",
     "mosaic_masked_logits_argmax_lse",
     "mosaic_logits_argmax_lse_workspace_bytes",
+    "mosaic_lazy_chunk_rows",
 )
 
 
@@ -71,6 +72,8 @@ def _load() -> ctypes.CDLL:
     lib.mosaic_masked_logits_argmax_lse.argtypes = [p, i64, i64, p, i64, p, i64, p, i64, st, st, p, p, p, p, i64, p]
     lib.mosaic_logits_argmax_lse_workspace_bytes.restype = i64
     lib.mosaic_logits_argmax_lse_workspace_bytes.argtypes = [i64, i64]
+    lib.mosaic_lazy_chunk_rows.restype = st
+    lib.mosaic_lazy_chunk_rows.argtypes = [i64, i64, st, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     return lib
 
 
@@ -131,6 +134,15 @@ def mosaic_logits_bytes(rows: int, V: int, dtype: torch.dtype) -> int:
 
 def mosaic_logits_variant(M: int, V: int, d: int, in_dtype: torch.dtype, out_dtype: torch.dtype) -> int:
     return int(lib.mosaic_logits_variant(int(M), int(V), int(d), _dtype_code(in_dtype), _dtype_code(out_dtype)))
+
+
+def mosaic_lazy_chunk_rows(M: int, V: int, dtype: torch.dtype, budget_bytes: int):
+    """(chunk_rows, num_chunks) of the lazy chunk choice for an [M, V] logits buffer of
+    `dtype` under `budget_bytes`; chunk_rows 0 means no chunking."""
+    c, k = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.mosaic_lazy_chunk_rows(int(M), int(V), _dtype_code(dtype), int(budget_bytes), ctypes.byref(c),
+                                      ctypes.byref(k)), "mosaic_lazy_chunk_rows")
+    return int(c.value), int(k.value)
 
 
 def mosaic_mask_compact(tokens: torch.Tensor, mask_id: int, idx: torch.Tensor | None = None,

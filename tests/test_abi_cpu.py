@@ -166,3 +166,31 @@ def test_argmax_lse_validation(m, kw, status):
 
 def test_argmax_lse_empty_is_ok_without_pointers(m):
     assert _argmax_lse(m, M=0, H=None, W=None, idx=None, rmax=None, rarg=None, rlse=None, ws=None, wsb=0) == 0
+
+
+def test_lazy_chunk_rows_matches_oracle(m):
+    import itertools
+
+    import torch
+
+    import oracle
+    for M, V in itertools.product((1, 2, 7, 33, 100, 257), (1, 5, 64)):
+        for dt, es in ((torch.bfloat16, 2), (torch.float32, 4)):
+            for budget in sorted({V * es, V * es + 1, 3 * V * es - 1, M * V * es - 1, M * V * es, 10 * M * V * es}):
+                if budget < V * es:
+                    continue
+                assert m.mosaic_lazy_chunk_rows(M, V, dt, budget) == oracle.lazy_chunk_rows(M, V, es, budget)
+    assert m.mosaic_lazy_chunk_rows(29491, 126464, torch.bfloat16, 4096 * 126464 * 2) == (3687, 8)
+    assert m.mosaic_lazy_chunk_rows(0, 10, torch.bfloat16, 0) == (0, 0)
+
+
+def test_lazy_chunk_rows_errors(m):
+    import ctypes
+    c, k = ctypes.c_int64(), ctypes.c_int64()
+    f = m.lib.mosaic_lazy_chunk_rows
+    assert f(10, 500, 1, 999, ctypes.byref(c), ctypes.byref(k)) == 2        # one row does not fit
+    assert f(-1, 500, 1, 999, ctypes.byref(c), ctypes.byref(k)) == 1
+    assert f(10, 500, 7, 10**9, ctypes.byref(c), ctypes.byref(k)) == 1      # unknown dtype
+    assert f(10, 500, 1, 10**9, None, ctypes.byref(k)) == 1
+    assert f(2**40, 2**30, 1, 2**62, ctypes.byref(c), ctypes.byref(k)) == 0  # M * V * esize overflows int64
+    assert c.value == 2**31 and k.value == 2**9
