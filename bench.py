@@ -16,6 +16,14 @@ go to stderr.
                achieved = (2*M*d*V of one step) / (GEMM time of one step), with the GEMM
                time measured by HIP events on the stream the kernels run on
   cpu_baseline the CPU oracle (fp64, OpenMP) timed on a bounded sample of rows
+
+--path selects what the step does after compaction (default: logits):
+  logits        the bf16 logits of every masked row, stored ([M, V])
+  argmax_lse    each masked row reduced in the kernel to (max, first argmax,
+                log-sum-exp); no logits buffer exists
+  dense_select  the baseline the pages contrast with: logits of all L rows with the
+                same kernel and chunking, then the masked rows copied out; `value`
+                still counts only 2*M*d*V, so it compares directly with `logits`
 """
 from __future__ import annotations
 
@@ -39,10 +47,17 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the gather-GEMM sources with comments and blank lines removed, so that
+    a measured traffic figure stays attached to the code it was measured on."""
+    import re
     h = hashlib.sha256()
-    for f in ("gather_gemm.hip", "mosaic_abi.cpp"):
-        with open(os.path.join(ROOT, "mask_only_logits_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in ("gather_gemm.hip", "mosaic_abi.cpp", "launch.h"):
+        with open(os.path.join(ROOT, "mask_only_logits_amd", "csrc", f), encoding="utf-8") as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            line = line.split("//", 1)[0].rstrip()
+            if line.strip():
+                h.update(line.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
@@ -176,9 +191,12 @@ def main():
                          "(a kernel of known traffic that calibrates rocprofv3's FETCH_SIZE/WRITE_SIZE)")
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="summarize rocprofv3 CSV output found under DIR into profiles/ and exit")
-    ap.add_argument("--path", choices=("logits", "argmax_lse"), default="logits",
+    ap.add_argument("--path", choices=("logits", "argmax_lse", "dense_select"), default="logits",
                     help="logits: store the bf16 logits of every masked row (default); argmax_lse: reduce each "
-                         "row to (max, first argmax, log-sum-exp) inside the kernel and store no logits")
+                         "row to (max, first argmax, log-sum-exp) inside the kernel and store no logits; "
+                         "dense_select: the baseline the pages contrast with -- logits of ALL L rows with the "
+                         "same kernel and chunking, then the masked rows copied out (value counts only the "
+                         "masked rows' 2*M*d*V, so it compares directly with the logits path)")
     args = ap.parse_args()
 
     if args.summarize_profile:
@@ -223,7 +241,17 @@ def main():
     flop = 2.0 * M * d * V
     rows_per_launch = M if launches == 1 else C
     consumer = args.path == "argmax_lse"
-    if consumer:
+    dense = args.path == "dense_select"
+    if dense:
+        out = torch.empty((M, V), dtype=out_dtype, device=dev)
+        full = torch.empty((L, V), dtype=out_dtype, device=dev)
+        all_rows = torch.arange(L, dtype=torch.int32, device=dev)
+        sel = torch.empty(M, dtype=torch.int64, device=dev)
+        launches = mosaic.mosaic_num_chunks(L, C)
+        variant = mosaic.mosaic_logits_variant(L if launches == 1 else C, V, d, H.dtype, out_dtype)
+        log(f"[bench] M={M} L={L} chunk_rows={C} launches={launches} path=dense_select variant={variant} "
+            f"peak logits={(full.numel() + out.numel()) * out.element_size() / 1e9:.2f} GB")
+    elif consumer:
         if wl.dtype != "bf16" or d % 64:
             log(f"[bench] the argmax_lse path needs bf16 inputs and d % 64 == 0 ({args.workload} has not)")
             sys.exit(2)
@@ -260,6 +288,10 @@ def main():
         if consumer:
             mosaic.mosaic_masked_logits_argmax_lse(H, idx, W, M=m, chunk_rows=C, row_max=rmax, row_argmax=rarg,
                                                    row_lse=rlse, workspace=ws, stream=stream)
+        elif dense:
+            mosaic.mosaic_masked_logits(H, all_rows, W, M=L, out=full, chunk_rows=C, stream=stream)
+            sel.copy_(idx[:m])
+            torch.index_select(full, 0, sel, out=out)
         else:
             mosaic.mosaic_masked_logits(H, idx, W, M=m, out=out, chunk_rows=C, stream=stream)
         if i is not None:
@@ -279,7 +311,8 @@ def main():
     compact_ms = [a[0].elapsed_time(a[1]) for a in ev]
     gemm_avg = float(np.mean(gemm_ms))
     value = flop / (ms_per_step / 1e3) / 1e12
-    achieved = flop / (gemm_avg / 1e3) / 1e12
+    # the kernel's own FLOP: the dense baseline multiplies all L rows
+    achieved = (2.0 * L * d * V if dense else flop) / (gemm_avg / 1e3) / 1e12
     log(f"[bench] {ms_per_step:.3f} ms/step ({value:.1f} TFLOP/s); GEMM {gemm_avg:.3f} ms/step "
         f"(min {min(gemm_ms):.3f}) = {achieved:.1f} TFLOP/s = {achieved / PEAK_BF16_TFLOPS:.1%} of bf16 peak; "
         f"{gemm_avg / launches:.3f} ms per launch; compaction+readback {np.mean(compact_ms) * 1e3:.1f} us")
@@ -287,6 +320,9 @@ def main():
     esize_in = 2 if wl.dtype == "bf16" else 4
     out_bytes = M * 12 if consumer else M * V * out.element_size()
     alg_bytes = launches * V * d * esize_in + M * d * esize_in + out_bytes + M * 4
+    if dense:
+        # the dense baseline's own work: all L rows
+        alg_bytes = launches * V * d * esize_in + L * d * esize_in + (L + 2 * M) * V * out.element_size()
     traffic = measured_traffic(args.workload, args.path)
     kernel = "gather_gemm_bf16_defer_kernel" if consumer else {0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel", 6: "gather_gemm_lowm_kernel",
               9: "gather_gemm_bf16_persist_kernel", 10: "gather_gemm_bf16_persist_kernel",
@@ -322,7 +358,11 @@ def main():
                    "accumulate": "fp32", "path": args.path},
         "roofline": roofline,
         "detail": {"gemm_ms_per_step": round(gemm_avg, 4), "gemm_ms_min": round(min(gemm_ms), 4),
-                   "compaction_readback_us": round(float(np.mean(compact_ms)) * 1e3, 2)},
+                   "compaction_readback_us": round(float(np.mean(compact_ms)) * 1e3, 2),
+                   # logits buffers alive at once: [L, V] + the selected [M, V] (dense_select),
+                   # the [M, V] output (logits), none (argmax_lse)
+                   "peak_logits_bytes": int((L * V + M * V) * out.element_size()) if dense else
+                   (0 if consumer else int(M * V * out.element_size()))},
     }
     if args.profile_copy_mib:
         n = args.profile_copy_mib * (1 << 20) // 4
