@@ -67,6 +67,14 @@ def _load():
                                                              _p, _p, _p]
         lib.oracle_lazy_chunk_rows.restype = ctypes.c_int
         lib.oracle_lazy_chunk_rows.argtypes = [_i64, _i64, _i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.oracle_quantize_rows_e4m3.restype = ctypes.c_int
+        lib.oracle_quantize_rows_e4m3.argtypes = [_p, _i64, _i64, ctypes.c_int, _p, _i64, _p, _p]
+        lib.oracle_logits_fp8.restype = ctypes.c_int
+        lib.oracle_logits_fp8.argtypes = [_p, _p, _i64, _p, _p, _i64, _i64, _p, _i64, _p]
         lib.oracle_logits_bytes.restype = _i64
         lib.oracle_logits_bytes.argtypes = [_i64, _i64, _i64]
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -206,6 +214,63 @@ def masked_logits_argmax_lse(H, idx, W, rows=None):
     if rc != 0:
         raise ValueError("empty vocabulary or out of memory")
     return mx, am, lse
+
+
+def e4m3_value(code: int) -> float:
+    """Value of an OCP FP8 E4M3 code."""
+    return float(_load().oracle_e4m3_value(int(code)))
+
+
+def e4m3_encode(x: float) -> int:
+    """Nearest E4M3 code of an fp32 value (ties to even, saturating at +-448)."""
+    return int(_load().oracle_e4m3_encode(float(np.float32(x))))
+
+
+def quantize_rows_e4m3(X, row_idx=None):
+    """Per-row E4M3 quantization of X [n, d] (bf16 or fp32, CPU tensor or array):
+    returns (codes uint8 [rows, d], scales float32 [rows]); rows = row_idx (gathered)
+    or all n rows."""
+    import torch
+    is_bf16 = (isinstance(X, torch.Tensor) and X.dtype == torch.bfloat16) or \
+              (isinstance(X, np.ndarray) and X.dtype == np.uint16)
+    x = _np(X, np.uint16 if is_bf16 else np.float32)
+    n, d = x.shape
+    ri = None if row_idx is None else _np(row_idx, np.int32)
+    rows = n if ri is None else ri.size
+    q = np.empty((rows, d), np.uint8)
+    sc = np.empty(rows, np.float32)
+    if rows == 0:
+        return q, sc
+    rc = _load().oracle_quantize_rows_e4m3(_ptr(x), n, d, int(is_bf16), None if ri is None else _ptr(ri), rows,
+                                           _ptr(q), _ptr(sc))
+    if rc != 0:
+        raise IndexError("row index out of range")
+    return q, sc
+
+
+def logits_fp8(qh, scale_h, qw, scale_w, rows=None) -> np.ndarray:
+    """fp64 logits of quantized rows: (sum_k qh[r, k] qw[v, k]) * scale_h[r] * scale_w[v]."""
+    qh = np.ascontiguousarray(qh, np.uint8)
+    qw = np.ascontiguousarray(qw, np.uint8)
+    sh = np.ascontiguousarray(scale_h, np.float32)
+    sw = np.ascontiguousarray(scale_w, np.float32)
+    M, d = qh.shape
+    V = qw.shape[0]
+    r = np.arange(M, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    out = np.empty((r.size, V), np.float64)
+    if r.size == 0 or V == 0:
+        return out
+    rc = _load().oracle_logits_fp8(_ptr(qh), _ptr(sh), M, _ptr(qw), _ptr(sw), V, d, _ptr(r), r.size, _ptr(out))
+    if rc != 0:
+        raise IndexError("row out of range")
+    return out
+
+
+def masked_logits_fp8(H, idx, W, rows=None) -> np.ndarray:
+    """The FP8 LM head on the masked rows: quantize H[idx] and W per row, then logits_fp8."""
+    qh, sh = quantize_rows_e4m3(H, idx)
+    qw, sw = quantize_rows_e4m3(W)
+    return logits_fp8(qh, sh, qw, sw, rows)
 
 
 def masked_logits_chunked(H, idx, W, chunk_rows: int) -> np.ndarray:

@@ -35,6 +35,18 @@
  *      1, 2, ... and stops at the first k whose largest chunk, ceil(M / k) rows, fits
  *      the byte budget; the chunks are then ceil(M / k) rows each (the last shorter).
  *
+ *  (5) FP8 LM head -- "扩散大语言模型内存优化：从理论到系统设计", §5 names combining the
+ *      logits micro-batching with FP8 quantization as a next step, without a scheme.
+ *      The plainest reading: OCP FP8 E4M3 codes (4 exponent bits, bias 7, 3 mantissa
+ *      bits, largest finite value 448, subnormals 2^-9 apart) with one fp32 scale per
+ *      row of W and per masked row of H.  A row x is quantized as
+ *          amax = max_k |x_k|, scale = amax / 448, q_k = RNE_e4m3(x_k * (448 / amax))
+ *      with each fp32 operation rounded to nearest even (a zero row gives zero codes
+ *      and scale 0).  The logits are the exact dot product of the decoded codes times
+ *      both row scales: out[i, v] = (sum_k q_h[i][k] q_w[v][k]) * scale_h[i] * scale_w[v],
+ *      in fp64 (products of E4M3 values are exact, and 4096-term sums of them fit in
+ *      the 53-bit significand).
+ *
  *  (4) per-row consumer -- what the sampler reads from a masked row's logits z[v]:
  *      the largest logit, the first vocabulary index that attains it (greedy
  *      decoding), and log(sum_v exp z[v]), from which the softmax confidence of any
@@ -281,6 +293,114 @@ int oracle_masked_logits_argmax_lse_bf16(const uint16_t *H, int64_t L, int64_t d
         free(z);
     }
     return failed ? -2 : 0;
+}
+
+/* ----------------------------------------------------------- (5) FP8 LM head */
+
+/* Value of an OCP FP8 E4M3 code: sign bit 7, exponent bits 6..3 (bias 7), mantissa
+ * bits 2..0; exponent 0 is subnormal (m/8 * 2^-6); exponent 15 with mantissa 7 is NaN. */
+double oracle_e4m3_value(uint8_t c)
+{
+    const double sgn = (c & 0x80) ? -1.0 : 1.0;
+    const int e = (c >> 3) & 0xF, m = c & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        return sgn * ldexp((double)m / 8.0, -6);
+    return sgn * ldexp(1.0 + (double)m / 8.0, e - 7);
+}
+
+/* Nearest E4M3 code to x (ties to the code with an even mantissa), saturating at
+ * +-448; NaN gives the NaN code.  The candidates are enumerated: the finite positive
+ * codes 0x00..0x7E are increasing in value. */
+uint8_t oracle_e4m3_encode(float x)
+{
+    if (isnan(x))
+        return 0x7F;
+    const uint8_t sgn = signbit(x) ? 0x80 : 0x00;
+    const double a = fabs((double)x);
+    int best = 0;
+    double best_d = a;               /* distance to code 0 */
+    for (int c = 1; c <= 0x7E; ++c) {
+        const double d = fabs(oracle_e4m3_value((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(sgn | best);
+}
+
+static float row_value(const void *X, int in_bf16, int64_t off)
+{
+    if (in_bf16) {
+        uint32_t u = (uint32_t)((const uint16_t *)X)[off] << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return f;
+    }
+    return ((const float *)X)[off];
+}
+
+/* Quantize `rows` rows of X ([*, d], bf16 when in_bf16 else fp32) to E4M3 codes q
+ * ([rows, d]) and fp32 scales.  Row r is source row row_idx[r] (or r when row_idx is
+ * NULL).  Returns 0, or -1 for a source row outside [0, nsrc). */
+int oracle_quantize_rows_e4m3(const void *X, int64_t nsrc, int64_t d, int in_bf16, const int32_t *row_idx,
+                              int64_t rows, uint8_t *q, float *scale)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t src = row_idx ? (int64_t)row_idx[r] : r;
+        if (src < 0 || src >= nsrc)
+            return -1;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t src = row_idx ? (int64_t)row_idx[r] : r;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < d; ++k) {
+            const float a = fabsf(row_value(X, in_bf16, src * d + k));
+            if (a > amax)
+                amax = a;
+        }
+        if (amax == 0.0f) {
+            memset(q + r * d, 0, (size_t)d);
+            scale[r] = 0.0f;
+            continue;
+        }
+        const volatile float inv = 448.0f / amax;    /* one fp32 division, rounded */
+        scale[r] = amax / 448.0f;
+        for (int64_t k = 0; k < d; ++k) {
+            const volatile float y = row_value(X, in_bf16, src * d + k) * inv;   /* fp32 product */
+            q[r * d + k] = oracle_e4m3_encode(y);
+        }
+    }
+    return 0;
+}
+
+/* out[r][v] = (sum_k value(qh[rows[r]][k]) * value(qw[v][k])) * scale_h[rows[r]] * scale_w[v]
+ * for the quantized rows qh ([M, d]) and qw ([V, d]); fp64, ascending k.  Returns 0,
+ * or -1 for a row outside [0, M). */
+int oracle_logits_fp8(const uint8_t *qh, const float *scale_h, int64_t M, const uint8_t *qw,
+                      const float *scale_w, int64_t V, int64_t d, const int64_t *rows, int64_t nrows,
+                      double *out)
+{
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= M)
+            return -1;
+    double lut[256];
+    for (int c = 0; c < 256; ++c)
+        lut[c] = oracle_e4m3_value((uint8_t)c);
+    const int64_t total = nrows * V;
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < total; ++e) {
+        const int64_t r = e / V, v = e % V;
+        const uint8_t *a = qh + rows[r] * d, *b = qw + v * d;
+        double acc = 0.0;
+        for (int64_t k = 0; k < d; ++k)
+            acc += lut[a[k]] * lut[b[k]];
+        out[e] = acc * (double)scale_h[rows[r]] * (double)scale_w[v];
+    }
+    return 0;
 }
 
 /* Number of OpenMP threads the logits loops run on (1 when built without OpenMP). */
