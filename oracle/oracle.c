@@ -311,22 +311,31 @@ double oracle_e4m3_value(uint8_t c)
 }
 
 /* Nearest E4M3 code to x (ties to the code with an even mantissa), saturating at
- * +-448; NaN gives the NaN code.  The candidates are enumerated: the finite positive
- * codes 0x00..0x7E are increasing in value. */
+ * +-448; NaN gives the NaN code.  The finite non-negative codes 0x00..0x7E are
+ * increasing in value, so the nearest one is found by bisection for the first code
+ * not below |x| and a comparison with the code before it. */
 uint8_t oracle_e4m3_encode(float x)
 {
     if (isnan(x))
         return 0x7F;
     const uint8_t sgn = signbit(x) ? 0x80 : 0x00;
     const double a = fabs((double)x);
-    int best = 0;
-    double best_d = a;               /* distance to code 0 */
-    for (int c = 1; c <= 0x7E; ++c) {
-        const double d = fabs(oracle_e4m3_value((uint8_t)c) - a);
-        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
-            best = c;
-            best_d = d;
-        }
+    if (a >= 448.0)
+        return (uint8_t)(sgn | 0x7E);
+    int lo = 0, hi = 0x7E;           /* value(hi) >= a */
+    while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if (oracle_e4m3_value((uint8_t)mid) < a)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    int best = lo;
+    if (lo > 0) {
+        const double up = oracle_e4m3_value((uint8_t)lo) - a;
+        const double down = a - oracle_e4m3_value((uint8_t)(lo - 1));
+        if (down < up || (down == up && ((lo - 1) & 1) == 0))
+            best = lo - 1;
     }
     return (uint8_t)(sgn | best);
 }
