@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "mask-only logits TFLOP/s (2·M·d·V) and % bf16 MFMA peak at L=32k, d=4096"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 
 
 def log(*a):
@@ -191,12 +192,13 @@ def main():
                          "(a kernel of known traffic that calibrates rocprofv3's FETCH_SIZE/WRITE_SIZE)")
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="summarize rocprofv3 CSV output found under DIR into profiles/ and exit")
-    ap.add_argument("--path", choices=("logits", "argmax_lse", "dense_select"), default="logits",
+    ap.add_argument("--path", choices=("logits", "argmax_lse", "dense_select", "fp8"), default="logits",
                     help="logits: store the bf16 logits of every masked row (default); argmax_lse: reduce each "
                          "row to (max, first argmax, log-sum-exp) inside the kernel and store no logits; "
                          "dense_select: the baseline the pages contrast with -- logits of ALL L rows with the "
                          "same kernel and chunking, then the masked rows copied out (value counts only the "
-                         "masked rows' 2*M*d*V, so it compares directly with the logits path)")
+                         "masked rows' 2*M*d*V, so it compares directly with the logits path); fp8: the FP8 "
+                         "(E4M3, per-row scales) LM head with W quantized beforehand")
     args = ap.parse_args()
 
     if args.summarize_profile:
@@ -242,7 +244,19 @@ def main():
     rows_per_launch = M if launches == 1 else C
     consumer = args.path == "argmax_lse"
     dense = args.path == "dense_select"
-    if dense:
+    fp8 = args.path == "fp8"
+    if fp8:
+        if wl.dtype != "bf16" or d % 128:
+            log(f"[bench] the fp8 path needs bf16 inputs and d % 128 == 0 ({args.workload} has not)")
+            sys.exit(2)
+        out = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
+        Wq, wsc = mosaic.mosaic_quantize_rows_fp8(W)          # the weights, quantized once
+        ws8 = torch.empty(mosaic.mosaic_logits_fp8_workspace_bytes(rows_per_launch, d), dtype=torch.uint8,
+                          device=dev)
+        variant = None
+        log(f"[bench] M={M} chunk_rows={C} launches={launches} path=fp8 (E4M3 per-row scales) "
+            f"out={out.numel() * 2 / 1e9:.2f} GB")
+    elif dense:
         out = torch.empty((M, V), dtype=out_dtype, device=dev)
         full = torch.empty((L, V), dtype=out_dtype, device=dev)
         all_rows = torch.arange(L, dtype=torch.int32, device=dev)
@@ -288,6 +302,9 @@ def main():
         if consumer:
             mosaic.mosaic_masked_logits_argmax_lse(H, idx, W, M=m, chunk_rows=C, row_max=rmax, row_argmax=rarg,
                                                    row_lse=rlse, workspace=ws, stream=stream)
+        elif fp8:
+            mosaic.mosaic_masked_logits_fp8(H, idx, Wq, wsc, M=m, out=out, chunk_rows=C, workspace=ws8,
+                                            stream=stream)
         elif dense:
             mosaic.mosaic_masked_logits(H, all_rows, W, M=L, out=full, chunk_rows=C, stream=stream)
             sel.copy_(idx[:m])
@@ -314,17 +331,22 @@ def main():
     # the kernel's own FLOP: the dense baseline multiplies all L rows
     achieved = (2.0 * L * d * V if dense else flop) / (gemm_avg / 1e3) / 1e12
     log(f"[bench] {ms_per_step:.3f} ms/step ({value:.1f} TFLOP/s); GEMM {gemm_avg:.3f} ms/step "
-        f"(min {min(gemm_ms):.3f}) = {achieved:.1f} TFLOP/s = {achieved / PEAK_BF16_TFLOPS:.1%} of bf16 peak; "
+        f"(min {min(gemm_ms):.3f}) = {achieved:.1f} TFLOP/s = "
+        f"{achieved / (PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS):.1%} of {'fp8' if fp8 else 'bf16'} peak; "
         f"{gemm_avg / launches:.3f} ms per launch; compaction+readback {np.mean(compact_ms) * 1e3:.1f} us")
 
     esize_in = 2 if wl.dtype == "bf16" else 4
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     out_bytes = M * 12 if consumer else M * V * out.element_size()
     alg_bytes = launches * V * d * esize_in + M * d * esize_in + out_bytes + M * 4
+    if fp8:
+        # W codes once per chunk + gathered H rows (bf16, quantized per chunk) + codes + out
+        alg_bytes = launches * V * d + M * d * 2 + M * V * 2 + M * 4
     if dense:
         # the dense baseline's own work: all L rows
         alg_bytes = launches * V * d * esize_in + L * d * esize_in + (L + 2 * M) * V * out.element_size()
     traffic = measured_traffic(args.workload, args.path)
-    kernel = "gather_gemm_bf16_defer_kernel" if consumer else {0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel", 6: "gather_gemm_lowm_kernel",
+    kernel = "gather_gemm_fp8_kernel" if fp8 else "gather_gemm_bf16_defer_kernel" if consumer else {0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel", 6: "gather_gemm_lowm_kernel",
               9: "gather_gemm_bf16_persist_kernel", 10: "gather_gemm_bf16_persist_kernel",
               11: "gather_gemm_bf16_persist_kernel", 15: "gather_gemm_bf16_defer_kernel",
               16: "gather_gemm_bf16_defer_kernel", 17: "gather_gemm_bf16_defer_kernel"}.get(variant, "gather_gemm_bf16_kernel")
@@ -334,8 +356,8 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(achieved_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), "traffic": traffic}
     roofline.update({"kernel": kernel, "launch_ms_avg": round(gemm_avg / launches, 4),
                      "algorithmic_bytes_per_launch": int(alg_bytes / launches),
                      "algorithmic_flop_per_launch": int(flop / launches)})
@@ -350,7 +372,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "dtype": "fp8 (e4m3)" if fp8 else ("bf16" if wl.dtype == "bf16" else "f32"),
         "data": "synthetic (seeded Gaussian H ~ N(0,1), W ~ N(0,0.02); uniform masked positions)",
         "config": {"workload": args.workload, "L": L, "d": d, "V": V, "M": M, "chunk_rows": C,
                    "launches_per_step": launches, "in_dtype": wl.dtype,
@@ -374,6 +396,9 @@ def main():
         del src, dst
         log(f"[bench] copy probe: 3 x {args.profile_copy_mib} MiB read + write")
 
+    if fp8 and not args.no_cpu_baseline:
+        log("[bench] no cpu_baseline on the fp8 path (its oracle would first quantize all of W)")
+        args.no_cpu_baseline = True
     if not args.no_cpu_baseline:
         idx_np = idx[:M].cpu().numpy()
         log("[bench] timing the CPU oracle on a row sample ...")

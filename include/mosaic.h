@@ -167,6 +167,45 @@ mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_
  * on a negative size or int64 overflow. */
 int64_t mosaic_logits_argmax_lse_workspace_bytes(int64_t rows, int64_t V);
 
+/* ---------------------------------------------------------- FP8 LM head --- */
+
+/* FP8 form of the logits step ([DS] §5 names combining the logits micro-batching with
+ * FP8 quantization as a next step; the scheme below is this library's reading).  Codes
+ * are OCP FP8 E4M3 (bias 7, 3 mantissa bits, largest finite value 448) with one fp32
+ * scale per row:  amax = max_k |x_k|,  scale = amax / 448,  q_k = RNE(x_k * (448/amax)),
+ * each fp32 operation rounded to nearest even; a zero row gives zero codes and scale 0.
+ *
+ * mosaic_quantize_rows_fp8: rows r < rows of X ([nsrc, d], in_dtype BF16 or F32,
+ * row-major, 16-byte aligned) -- source row row_idx[r] (device int32, values in
+ * [0, nsrc); a caller contract) or r when row_idx is NULL -- to q ([rows, d] uint8,
+ * 16-byte aligned) and scale (float[rows]).  Used once for W.  d % 8 == 0, else
+ * UNSUPPORTED.  rows == 0 or d == 0: OK, nothing enqueued. */
+mosaic_status_t mosaic_quantize_rows_fp8(const void *X, int64_t nsrc, int64_t d, mosaic_dtype_t in_dtype,
+                                         const int32_t *row_idx, int64_t rows, uint8_t *q, float *scale,
+                                         void *stream);
+
+/* Workspace bytes of mosaic_masked_logits_fp8 for chunks of `rows` rows:
+ * rows * d rounded up to 16, plus 4 * rows; -1 on a negative size or overflow. */
+int64_t mosaic_logits_fp8_workspace_bytes(int64_t rows, int64_t d);
+
+/* out[i, v] = (sum_k q_h[i][k] * Wq[v][k]) * scale_h[i] * w_scale[v], rounded to bf16, for
+ * i < M, v < V, where q_h[i], scale_h[i] quantize row H[idx[i]] as above.  Each chunk
+ * quantizes its rows into `workspace` (gathered through idx; H itself is not copied),
+ * then runs one fp8 MFMA GEMM (fp32 accumulation) launch.
+ *   H        [L, d] bf16 row-major, 16-byte aligned;  idx int32[M] in [0, L).
+ *   Wq       [V, d] E4M3 codes and w_scale float[V] (16-byte aligned), from
+ *            mosaic_quantize_rows_fp8 on W.
+ *   out      [M, V] bf16 (out_dtype must be BF16), 16-byte aligned.
+ *   chunk_rows, stream: as for mosaic_masked_logits.
+ *   workspace >= mosaic_logits_fp8_workspace_bytes(C, d) bytes, C = the rows of the
+ *            largest chunk; 16-byte aligned; contents undefined on return.
+ * d % 128 == 0 (else UNSUPPORTED).  M == 0 or V == 0: OK, nothing enqueued.  Results
+ * do not depend on chunk_rows. */
+mosaic_status_t mosaic_masked_logits_fp8(const void *H, int64_t L, int64_t d, const int32_t *idx, int64_t M,
+                                         const uint8_t *Wq, const float *w_scale, int64_t V, void *out,
+                                         int64_t chunk_rows, mosaic_dtype_t out_dtype, void *workspace,
+                                         int64_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------ host helpers --- */
 
 /* Number of chunks a call of mosaic_masked_logits makes for M rows ([DS] §3.2.2):

@@ -11,7 +11,7 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libmosaic.so"
-SOURCES = ["compact.hip", "gather_gemm.hip", "mosaic_abi.cpp"]
+SOURCES = ["compact.hip", "gather_gemm.hip", "gather_gemm_fp8.hip", "mosaic_abi.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall",

@@ -1,0 +1,375 @@
+// FP8 (OCP E4M3) LM head for the mask-only logits path.
+//
+// "扩散大语言模型内存优化：从理论到系统设计", §5 names combining the logits micro-batching
+// with FP8 quantization as a next step.  Here: W is quantized once, per vocabulary row,
+// and the masked rows of H are quantized per row as each chunk runs; one fp32 scale per
+// row, scale = amax / 448, codes = RNE(x * (448 / amax)).  The logits are the fp32 dot
+// product of the codes (gfx950 fp8 MFMA) times both row scales, rounded to bf16.
+//
+//  * quantize_rows_e4m3_kernel: one wave per row (gathered through an index list when
+//    given).  Pass 1: |x| max over the row, reduced across the wave.  Pass 2 (the row is
+//    in L2 by then): y = x * inv in fp32, then v_cvt_pk_fp8_f32 (round to nearest even;
+//    |y| <= 448 by construction, so it never reaches the non-finite codes).
+//  * gather_gemm_fp8_kernel: the bf16 tiled kernel's structure with fp8 operands.  A
+//    256 x 256 output tile per workgroup; K tiles of 128 codes, i.e. 128-byte rows, so
+//    the DMA (global_load_lds_dwordx4), the two 64 KiB LDS stages and the XOR swizzle
+//    are the bf16 kernel's.  Each 64-deep k sub-step is one
+//    v_mfma_scale_f32_32x32x64_f8f6f4 per 32 x 32 block with unit block scales (E8M0
+//    127), which is the plain fp8 product; a lane supplies 32 codes of its row (two
+//    16-byte LDS reads).  The epilogue multiplies each fp32 sum by the row scale of H
+//    and the row scale of W.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "launch.h"
+
+namespace mosaic {
+namespace {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt vmcnt(N) lgkmcnt(0)
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0x0 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void bar()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+template <bool IN_BF16>
+__device__ __forceinline__ void load8(const void *X, int64_t off, float (&x)[8])
+{
+    if constexpr (IN_BF16) {
+        const uint4 u = *(const uint4 *)((const uint16_t *)X + off);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+            x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+        }
+    } else {
+        const f32x4_t a = *(const f32x4_t *)((const float *)X + off);
+        const f32x4_t b = *(const f32x4_t *)((const float *)X + off + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = a[i];
+            x[4 + i] = b[i];
+        }
+    }
+}
+
+// Row r of the output is source row row_idx[r] (or r).  d % 8 == 0.
+template <bool IN_BF16>
+__global__ __launch_bounds__(256) void quantize_rows_e4m3_kernel(const void *__restrict__ X, int32_t d,
+                                                                const int32_t *__restrict__ row_idx,
+                                                                int64_t rows, uint8_t *__restrict__ q,
+                                                                float *__restrict__ scale)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows)
+        return;
+    const int64_t src = row_idx ? (int64_t)row_idx[r] : r;
+    const int64_t base = src * d;
+    float amax = 0.0f;
+    for (int k = lane * 8; k < d; k += 512) {
+        float x[8];
+        load8<IN_BF16>(X, base + k, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            amax = fmaxf(amax, fabsf(x[i]));
+    }
+    amax = wave_max(amax);
+    uint8_t *qr = q + r * d;
+    if (amax == 0.0f) {
+        for (int k = lane * 8; k < d; k += 512)
+            *(uint2 *)(qr + k) = make_uint2(0u, 0u);
+        if (lane == 0)
+            scale[r] = 0.0f;
+        return;
+    }
+    const float inv = 448.0f / amax;
+    for (int k = lane * 8; k < d; k += 512) {
+        float x[8];
+        load8<IN_BF16>(X, base + k, x);
+        uint32_t w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            int p = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h] * inv, x[4 * h + 1] * inv, 0, false);
+            p = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h + 2] * inv, x[4 * h + 3] * inv, p, true);
+            w[h] = (uint32_t)p;
+        }
+        *(uint2 *)(qr + k) = make_uint2(w[0], w[1]);
+    }
+    if (lane == 0)
+        scale[r] = amax / 448.0f;
+}
+
+// logits[i, v] = (sum_k Hq[i, k] Wq[v, k]) * hs[i] * ws[v] for i < rows, v < V; Hq holds
+// the chunk's quantized rows contiguously ([rows, d]); d % 128 == 0.
+template <int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW / 4, NW / 4))) void
+gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__ hs, int32_t rows,
+                       const uint8_t *__restrict__ Wq, const float *__restrict__ ws, int32_t V, int32_t d,
+                       __bf16 *__restrict__ out, int64_t ldo, int32_t group_m)
+{
+    constexpr int BV = 256, BM = 256, BK = 128, NSTAGE = 2, NSPREAD = 2;
+    constexpr int ROW_BYTES = BK;             // one byte per code
+    constexpr int CHUNKS = ROW_BYTES / 16, RPI = 64 / CHUNKS;
+    constexpr int W_TILE = BV * ROW_BYTES, H_TILE = BM * ROW_BYTES, STAGE = W_TILE + H_TILE;
+    constexpr int WV = BV / 2, WM = BM / (NW / 2);
+    constexpr int AV = WV / 32, AM = WM / 32;
+    constexpr int LW = BV / RPI / NW, LH = BM / RPI / NW;
+    constexpr int NSUB = BK / 64;             // MFMA k sub-steps per K tile (2)
+    constexpr int NDMA = LW + LH, PER = NDMA / NSPREAD;
+    static_assert(NDMA % NSPREAD == 0 && NSPREAD <= NSUB, "spread");
+
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+
+    const int nvt = (V + BV - 1) / BV;
+    const int nmt = (rows + BM - 1) / BM;
+    const int nblk = nvt * nmt;
+    // XCD-aware renumbering and grouped order, as in the bf16 tiled kernel
+    const int b = blockIdx.x;
+    const int qq = nblk >> 3, rem = nblk & 7, xcd = b & 7, slot = b >> 3;
+    const int t = (xcd < rem ? xcd * (qq + 1) : rem * (qq + 1) + (xcd - rem) * qq) + slot;
+    const int per_group = group_m * nvt;
+    const int g = t / per_group;
+    const int first_m = g * group_m;
+    const int gsz = min(nmt - first_m, group_m);
+    const int local = t - g * per_group;
+    const int m0 = (first_m + local % gsz) * BM;
+    const int v0 = (local / gsz) * BV;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wv = wave & 1, wm = wave >> 1;
+    auto swz = [](int r) { return (r >> 1) & 7; };
+
+    // DMA sources: lane i of instruction j fills tile row j*RPI + i/CHUNKS, physical
+    // chunk i%CHUNKS (logical chunk (i%CHUNKS) ^ swz(row)).  Rows past V / rows re-read
+    // the last valid row; their results are never stored.
+    const uint8_t *wsrc[LW];
+    const uint8_t *hsrc[LH];
+#pragma unroll
+    for (int j = 0; j < LW; ++j) {
+        const int r = (wave * LW + j) * RPI + lane / CHUNKS;
+        wsrc[j] = Wq + (int64_t)min(v0 + r, V - 1) * d + ((lane % CHUNKS) ^ swz(r)) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < LH; ++j) {
+        const int r = (wave * LH + j) * RPI + lane / CHUNKS;
+        hsrc[j] = Hq + (int64_t)min(m0 + r, rows - 1) * d + ((lane % CHUNKS) ^ swz(r)) * 16;
+    }
+    auto issue_part = [&](int so, int kt, int p) {
+        const int kb = kt * ROW_BYTES;
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            if (i / PER != p)
+                continue;
+            if (i < LW)
+                __builtin_amdgcn_global_load_lds((const void *)(wsrc[i] + kb),
+                                                 (lds_void_t *)(smem + so + (wave * LW + i) * 1024), 16, 0, 0);
+            else
+                __builtin_amdgcn_global_load_lds((const void *)(hsrc[i - LW] + kb),
+                                                 (lds_void_t *)(smem + so + W_TILE + (wave * LH + i - LW) * 1024),
+                                                 16, 0, 0);
+        }
+    };
+
+    f32x16_t acc[AV][AM];
+#pragma unroll
+    for (int a = 0; a < AV; ++a)
+#pragma unroll
+        for (int bm = 0; bm < AM; ++bm)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[a][bm][e] = 0.0f;
+
+    // Fragment of sub-step s: lane reads codes 64 s + 32 hi + (0..31) of row (lane & 31)
+    // of a 32-row block, i.e. logical chunks 4 s + 2 hi and 4 s + 2 hi + 1.
+    const int fr = lane & 31, hi = lane >> 5;
+    const int lane_chunk = ((2 * hi) ^ swz(fr)) * 16;
+    const int a_addr = (wv * WV + fr) * ROW_BYTES + lane_chunk;
+    const int b_addr = W_TILE + (wm * WM + fr) * ROW_BYTES + lane_chunk;
+    auto frag = [&](int addr, int s) {
+        const uint4 lo = *(const uint4 *)(smem + (addr ^ (64 * s)));
+        const uint4 up = *(const uint4 *)(smem + (addr ^ (64 * s + 16)));
+        return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)up.x, (int)up.y, (int)up.z, (int)up.w};
+    };
+    auto load_frags = [&](int so, int s, i32x8_t (&af)[AV], i32x8_t (&bf)[AM]) {
+#pragma unroll
+        for (int a = 0; a < AV; ++a)
+            af[a] = frag(a_addr + so + a * 32 * ROW_BYTES, s);
+#pragma unroll
+        for (int bm = 0; bm < AM; ++bm)
+            bf[bm] = frag(b_addr + so + bm * 32 * ROW_BYTES, s);
+    };
+    auto mma = [&](const i32x8_t (&af)[AV], const i32x8_t (&bf)[AM]) {
+#pragma unroll
+        for (int a = 0; a < AV; ++a)
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm)
+                acc[a][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[a], bf[bm], acc[a][bm], 0, 0, 0,
+                                                                             127, 0, 127);
+    };
+    constexpr int NFR = 2 * (AV + AM);
+    auto interleave = [&](int nvm) {
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            if (i < nvm) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NFR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+
+    // Pipeline as in the bf16 tiled kernel (two stages; the refill of the stage just
+    // read is split over the last sub-step of a step and the first of the next).
+    const int nk = d / BK;
+    i32x8_t af[2][AV], bf[2][AM];
+    const int npre = min(NSTAGE, nk);
+    for (int s = 0; s < npre; ++s)
+#pragma unroll
+        for (int p = 0; p < NSPREAD; ++p)
+            issue_part(s * STAGE, s, p);
+    if (npre == 2)
+        wait_vm<NDMA>();
+    else
+        wait_vm<0>();
+    bar();
+    load_frags(0, 0, af[0], bf[0]);
+    int rd = 0, kt = 0, pso = 0, pkt = 0;
+    bool pending = false;
+    for (; kt + NSTAGE < nk; ++kt) {
+        // sub-step 0: the rest of the previous refill, the fragments of sub-step 1
+        if (pending)
+            issue_part(pso, pkt, 1);
+        load_frags(rd, 1, af[1], bf[1]);
+        mma(af[0], bf[0]);
+        interleave(pending ? PER : 0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<0>();
+        bar();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_part(rd, kt + NSTAGE, 0);
+        pso = rd;
+        pkt = kt + NSTAGE;
+        pending = true;
+        const int nx = (rd + STAGE == NSTAGE * STAGE) ? 0 : rd + STAGE;
+        load_frags(nx, 0, af[0], bf[0]);
+        mma(af[1], bf[1]);
+        interleave(PER);
+        __builtin_amdgcn_sched_barrier(0);
+        rd = nx;
+    }
+    for (; kt < nk; ++kt) {
+        if (pending)
+            issue_part(pso, pkt, 1);
+        pending = false;
+        load_frags(rd, 1, af[1], bf[1]);
+        mma(af[0], bf[0]);
+        if (kt + 1 < nk) {
+            wait_vm<0>();
+            bar();
+            rd = (rd + STAGE == NSTAGE * STAGE) ? 0 : rd + STAGE;
+            load_frags(rd, 0, af[0], bf[0]);
+        }
+        mma(af[1], bf[1]);
+    }
+
+    // epilogue: lane holds vocabulary entries v0 + wv*WV + 32a + 8gq + 4hi + (0..3) of
+    // masked row m0 + wm*WM + 32bm + fr
+    const bool vec_ok = ((uintptr_t)out & 7) == 0 && (ldo & 3) == 0;
+#pragma unroll
+    for (int bm = 0; bm < AM; ++bm) {
+        const int row = m0 + wm * WM + bm * 32 + fr;
+        if (row >= rows)
+            continue;
+        const float h = hs[row];
+#pragma unroll
+        for (int a = 0; a < AV; ++a) {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int v = v0 + wv * WV + a * 32 + gq * 8 + hi * 4;
+                __bf16 *o = out + (int64_t)row * ldo + v;
+                if (vec_ok && v + 3 < V) {
+                    const f32x4_t w = *(const f32x4_t *)(ws + v);
+                    uint32_t p[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const __bf16 lo = static_cast<__bf16>(acc[a][bm][gq * 4 + 2 * e] * (h * w[2 * e]));
+                        const __bf16 up = static_cast<__bf16>(acc[a][bm][gq * 4 + 2 * e + 1] * (h * w[2 * e + 1]));
+                        p[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, up) << 16);
+                    }
+                    *(uint2 *)o = make_uint2(p[0], p[1]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (v + e < V)
+                            o[e] = static_cast<__bf16>(acc[a][bm][gq * 4 + e] * (h * ws[v + e]));
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows_e4m3(const void *X, bool in_bf16, int64_t d, const int32_t *row_idx, int64_t rows,
+                                     uint8_t *q, float *scale, hipStream_t stream)
+{
+    if (rows <= 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (in_bf16)
+        hipLaunchKernelGGL(quantize_rows_e4m3_kernel<true>, grid, dim3(256), 0, stream, X, (int32_t)d, row_idx, rows,
+                           q, scale);
+    else
+        hipLaunchKernelGGL(quantize_rows_e4m3_kernel<false>, grid, dim3(256), 0, stream, X, (int32_t)d, row_idx,
+                           rows, q, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8(const uint8_t *Hq, const float *hs, int64_t rows, const uint8_t *Wq, const float *ws,
+                           int64_t V, int64_t d, void *out, int64_t ldo, int group_m, int nwaves, hipStream_t stream)
+{
+    if (group_m <= 0)
+        group_m = kDefaultGroupM;
+    const int64_t nblk = ((V + 255) / 256) * ((rows + 255) / 256);
+    if (nwaves == 4)
+        hipLaunchKernelGGL(gather_gemm_fp8_kernel<4>, dim3((unsigned)nblk), dim3(256), 0, stream, Hq, hs,
+                           (int32_t)rows, Wq, ws, (int32_t)V, (int32_t)d, (__bf16 *)out, ldo, group_m);
+    else
+        hipLaunchKernelGGL(gather_gemm_fp8_kernel<8>, dim3((unsigned)nblk), dim3(512), 0, stream, Hq, hs,
+                           (int32_t)rows, Wq, ws, (int32_t)V, (int32_t)d, (__bf16 *)out, ldo, group_m);
+    return hipGetLastError();
+}
+
+}  // namespace mosaic

@@ -57,4 +57,15 @@ hipError_t launch_logits_argmax_lse(const void *H, const int32_t *idx, int64_t r
                                     float *row_max, int32_t *row_argmax, float *row_lse, int group_m,
                                     hipStream_t stream);
 
+// FP8 LM head.  Quantize `rows` rows of X ([*, d], bf16 or fp32, d % 8 == 0; row r is
+// source row row_idx[r], or r when row_idx is null) to E4M3 codes q ([rows, d]) and
+// fp32 row scales.
+hipError_t launch_quantize_rows_e4m3(const void *X, bool in_bf16, int64_t d, const int32_t *row_idx, int64_t rows,
+                                     uint8_t *q, float *scale, hipStream_t stream);
+
+// out[i, v] (bf16) = (sum_k Hq[i, k] Wq[v, k]) * hs[i] * ws[v] for i < rows, v < V;
+// d % 128 == 0; nwaves 4 or 8.
+hipError_t launch_gemm_fp8(const uint8_t *Hq, const float *hs, int64_t rows, const uint8_t *Wq, const float *ws,
+                           int64_t V, int64_t d, void *out, int64_t ldo, int group_m, int nwaves, hipStream_t stream);
+
 }  // namespace mosaic

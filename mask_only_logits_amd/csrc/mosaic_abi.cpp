@@ -38,11 +38,13 @@ int64_t checked_bytes(int64_t rows, int64_t V, int64_t esize)
     return n * esize;
 }
 
-// Debug/tuning override read on every call: MOSAIC_TUNE="variant=<n>,group_m=<g>".
+// Debug/tuning override read on every call:
+// MOSAIC_TUNE="variant=<n>,group_m=<g>,waves=<w>" (waves: the FP8 kernel's 8 or 4).
 // A forced variant that cannot run the call's shape is ignored.
 struct Tune {
     int variant = -1;
     int group_m = 0;
+    int waves = 8;   // FP8 kernel: two waves per SIMD measured 11% faster than one
 };
 
 Tune read_tune()
@@ -56,6 +58,8 @@ Tune read_tune()
         t.variant = atoi(p + 8);
     if ((p = strstr(e, "group_m=")))
         t.group_m = atoi(p + 8);
+    if ((p = strstr(e, "waves=")) && atoi(p + 6) == 4)
+        t.waves = 4;
     return t;
 }
 
@@ -324,6 +328,85 @@ mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_
                                                               parg, psum, row_max + r0, row_argmax + r0,
                                                               row_lse + r0, group_m, (hipStream_t)stream);
         if (e != hipSuccess)
+            return MOSAIC_ERR_DEVICE;
+    }
+    return MOSAIC_OK;
+}
+
+mosaic_status_t mosaic_quantize_rows_fp8(const void *X, int64_t nsrc, int64_t d, mosaic_dtype_t in_dtype,
+                                         const int32_t *row_idx, int64_t rows, uint8_t *q, float *scale,
+                                         void *stream)
+{
+    if (nsrc < 0 || d < 0 || rows < 0 || esize_of(in_dtype) == 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (rows == 0 || d == 0)
+        return MOSAIC_OK;
+    if (d % 8 != 0)
+        return MOSAIC_ERR_UNSUPPORTED;
+    if (!X || !q || !scale || nsrc == 0 || (!row_idx && rows > nsrc))
+        return MOSAIC_ERR_INVALID_ARG;
+    if (!aligned16(X) || !aligned16(q) || ((uintptr_t)scale & 3u) || ((uintptr_t)row_idx & 3u))
+        return MOSAIC_ERR_INVALID_ARG;
+    if (checked_bytes(nsrc, d, esize_of(in_dtype)) < 0 || checked_bytes(rows, d, 1) < 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (d > kMaxPos)
+        return MOSAIC_ERR_UNSUPPORTED;
+    return mosaic::launch_quantize_rows_e4m3(X, in_dtype == MOSAIC_BF16, d, row_idx, rows, q, scale,
+                                             (hipStream_t)stream) == hipSuccess
+               ? MOSAIC_OK
+               : MOSAIC_ERR_DEVICE;
+}
+
+int64_t mosaic_logits_fp8_workspace_bytes(int64_t rows, int64_t d)
+{
+    const int64_t codes = checked_bytes(rows, d, 1);
+    if (codes < 0 || rows < 0)
+        return -1;
+    const int64_t aligned = (codes + 15) / 16 * 16;
+    if (aligned > INT64_MAX - 4 * rows)
+        return -1;
+    return aligned + 4 * rows;
+}
+
+mosaic_status_t mosaic_masked_logits_fp8(const void *H, int64_t L, int64_t d, const int32_t *idx, int64_t M,
+                                         const uint8_t *Wq, const float *w_scale, int64_t V, void *out,
+                                         int64_t chunk_rows, mosaic_dtype_t out_dtype, void *workspace,
+                                         int64_t workspace_bytes, void *stream)
+{
+    if (M < 0 || V < 0 || L < 0 || d < 0 || esize_of(out_dtype) == 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (M == 0 || V == 0)
+        return MOSAIC_OK;
+    if (out_dtype != MOSAIC_BF16 || d % 128 != 0 || d > (1 << 22))
+        return MOSAIC_ERR_UNSUPPORTED;
+    if (!H || !idx || !Wq || !w_scale || !out || !workspace || L == 0 || d == 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (!aligned16(H) || !aligned16(Wq) || !aligned16(out) || !aligned16(workspace) || ((uintptr_t)idx & 3u) ||
+        ((uintptr_t)w_scale & 15u))
+        return MOSAIC_ERR_INVALID_ARG;
+    if (checked_bytes(M, V, 2) < 0 || checked_bytes(L, d, 2) < 0 || checked_bytes(V, d, 1) < 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (L > kMaxPos || V > kMaxPos || d > kMaxPos)
+        return MOSAIC_ERR_UNSUPPORTED;
+    const int64_t K = mosaic_num_chunks(M, chunk_rows);
+    const int64_t C = (K == 1) ? M : chunk_rows;
+    if (C > kMaxPos || ((C + 255) / 256) * ((V + 255) / 256) > 0x7fffffffLL)
+        return MOSAIC_ERR_UNSUPPORTED;
+    const int64_t need = mosaic_logits_fp8_workspace_bytes(C, d);
+    if (need < 0 || workspace_bytes < need)
+        return MOSAIC_ERR_INVALID_ARG;
+    // workspace: the chunk's codes [C, d], then its row scales [C]
+    uint8_t *hq = (uint8_t *)workspace;
+    float *hs = (float *)(hq + (C * d + 15) / 16 * 16);
+    const Tune t = read_tune();
+    for (int64_t k = 0; k < K; ++k) {
+        const int64_t r0 = k * C;
+        const int64_t r1 = (r0 + C < M) ? r0 + C : M;
+        void *chunk_out = (char *)out + r0 * V * 2;
+        if (mosaic::launch_quantize_rows_e4m3(H, true, d, idx + r0, r1 - r0, hq, hs, (hipStream_t)stream) !=
+                hipSuccess ||
+            mosaic::launch_gemm_fp8(hq, hs, r1 - r0, Wq, w_scale, V, d, chunk_out, V, t.group_m, t.waves,
+                                    (hipStream_t)stream) != hipSuccess)
             return MOSAIC_ERR_DEVICE;
     }
     return MOSAIC_OK;

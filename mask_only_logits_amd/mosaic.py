@@ -37,6 +37,9 @@ EXPORTS = (
     "mosaic_masked_logits_argmax_lse",
     "mosaic_logits_argmax_lse_workspace_bytes",
     "mosaic_lazy_chunk_rows",
+    "mosaic_quantize_rows_fp8",
+    "mosaic_logits_fp8_workspace_bytes",
+    "mosaic_masked_logits_fp8",
 )
 
 
@@ -72,6 +75,12 @@ def _load() -> ctypes.CDLL:
     lib.mosaic_masked_logits_argmax_lse.argtypes = [p, i64, i64, p, i64, p, i64, p, i64, st, st, p, p, p, p, i64, p]
     lib.mosaic_logits_argmax_lse_workspace_bytes.restype = i64
     lib.mosaic_logits_argmax_lse_workspace_bytes.argtypes = [i64, i64]
+    lib.mosaic_quantize_rows_fp8.restype = st
+    lib.mosaic_quantize_rows_fp8.argtypes = [p, i64, i64, st, p, i64, p, p, p]
+    lib.mosaic_logits_fp8_workspace_bytes.restype = i64
+    lib.mosaic_logits_fp8_workspace_bytes.argtypes = [i64, i64]
+    lib.mosaic_masked_logits_fp8.restype = st
+    lib.mosaic_masked_logits_fp8.argtypes = [p, i64, i64, p, i64, p, p, i64, p, i64, st, p, i64, p]
     lib.mosaic_lazy_chunk_rows.restype = st
     lib.mosaic_lazy_chunk_rows.argtypes = [i64, i64, st, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     return lib
@@ -272,3 +281,58 @@ def mosaic_masked_logits_argmax_lse(H: torch.Tensor, idx: torch.Tensor, W: torch
         _dev(row_lse, "row_lse", torch.float32), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         _stream(stream)), "mosaic_masked_logits_argmax_lse")
     return row_max, row_argmax, row_lse, out
+
+
+def mosaic_quantize_rows_fp8(X: torch.Tensor, row_idx: torch.Tensor | None = None, rows: int | None = None,
+                             q: torch.Tensor | None = None, scale: torch.Tensor | None = None, stream=None):
+    """Per-row OCP E4M3 quantization of X [n, d] (bf16 or fp32): returns (codes uint8
+    [rows, d], scales float32 [rows]); rows = len(row_idx) (gathered rows) or n."""
+    if X.dim() != 2:
+        raise ValueError("X must be [n, d]")
+    n, d = X.shape
+    if rows is None:
+        rows = n if row_idx is None else row_idx.numel()
+    if q is None:
+        q = torch.empty((rows, d), dtype=torch.uint8, device=X.device)
+    if scale is None:
+        scale = torch.empty(rows, dtype=torch.float32, device=X.device)
+    _check(lib.mosaic_quantize_rows_fp8(_dev(X, "X"), n, d, _dtype_code(X.dtype),
+                                        _dev(row_idx, "row_idx", torch.int32) if row_idx is not None else None,
+                                        int(rows), _dev(q, "q", torch.uint8), _dev(scale, "scale", torch.float32),
+                                        _stream(stream)), "mosaic_quantize_rows_fp8")
+    return q, scale
+
+
+def mosaic_logits_fp8_workspace_bytes(rows: int, d: int) -> int:
+    n = int(lib.mosaic_logits_fp8_workspace_bytes(int(rows), int(d)))
+    if n < 0:
+        raise ValueError("workspace size overflows")
+    return n
+
+
+def mosaic_masked_logits_fp8(H: torch.Tensor, idx: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor,
+                             M: int | None = None, out: torch.Tensor | None = None, chunk_rows: int = 0,
+                             workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """bf16 logits [M, V] of the FP8 LM head: H[idx[:M]] quantized per row on the fly,
+    times the pre-quantized W (Wq uint8 [V, d], w_scale float32 [V])."""
+    if H.dim() != 2 or Wq.dim() != 2 or H.shape[1] != Wq.shape[1]:
+        raise ValueError("H must be [L, d] and Wq [V, d]")
+    L, d = H.shape
+    V = Wq.shape[0]
+    M = idx.numel() if M is None else int(M)
+    if M > idx.numel():
+        raise ValueError("M exceeds the length of idx")
+    if out is None:
+        out = torch.empty((M, V), dtype=torch.bfloat16, device=H.device)
+    elif out.numel() < M * V:
+        raise ValueError("out is smaller than M * V")
+    C = M if chunk_rows <= 0 or chunk_rows >= M else int(chunk_rows)
+    if workspace is None:
+        workspace = torch.empty(max(16, mosaic_logits_fp8_workspace_bytes(C, d)), dtype=torch.uint8,
+                                device=H.device)
+    _check(lib.mosaic_masked_logits_fp8(_dev(H, "H", torch.bfloat16), L, d, _dev(idx, "idx", torch.int32), M,
+                                        _dev(Wq, "Wq", torch.uint8), _dev(w_scale, "w_scale", torch.float32), V,
+                                        _dev(out, "out"), int(chunk_rows), _dtype_code(out.dtype),
+                                        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                                        _stream(stream)), "mosaic_masked_logits_fp8")
+    return out

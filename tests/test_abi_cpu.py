@@ -21,7 +21,7 @@ def m():
 
 def test_exports_every_declared_symbol(m):
     hdr = open(os.path.join(ROOT, "include", "mosaic.h"), encoding="utf-8").read()
-    declared = set(re.findall(r"\b(mosaic_[a-z_]+)\s*\(", hdr))
+    declared = set(re.findall(r"\b(mosaic_[a-z0-9_]+)\s*\(", hdr))
     assert declared == set(m.EXPORTS)
     for name in declared:
         assert hasattr(m.lib, name), name
@@ -194,3 +194,55 @@ def test_lazy_chunk_rows_errors(m):
     assert f(10, 500, 1, 10**9, None, ctypes.byref(k)) == 1
     assert f(2**40, 2**30, 1, 2**62, ctypes.byref(c), ctypes.byref(k)) == 0  # M * V * esize overflows int64
     assert c.value == 2**31 and k.value == 2**9
+
+
+def test_fp8_workspace_bytes(m):
+    f = m.lib.mosaic_logits_fp8_workspace_bytes
+    assert f(4096, 4096) == 4096 * 4096 + 4 * 4096
+    assert f(3, 10) == 32 + 12
+    assert f(0, 10) == 0
+    assert f(-1, 10) == -1 and f(10, -1) == -1
+    assert f(2**62, 2**10) == -1
+
+
+def _quant(m, X=A16, n=100, d=64, i=1, ridx=None, rows=10, q=A16, sc=A16):
+    return m.lib.mosaic_quantize_rows_fp8(X, n, d, i, ridx, rows, q, sc, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), 1), (dict(d=-1), 1), (dict(rows=-1), 1), (dict(i=7), 1),
+    (dict(d=12), 2),                                   # d % 8 != 0
+    (dict(X=None), 1), (dict(q=None), 1), (dict(sc=None), 1),
+    (dict(X=A8), 1), (dict(q=A8), 1), (dict(sc=A16 + 2), 1), (dict(ridx=A16 + 1), 1),
+    (dict(rows=101), 1),                               # more rows than the source without an index list
+    (dict(n=2**40, d=2**30), 1),
+])
+def test_quantize_fp8_validation(m, kw, status):
+    assert _quant(m, **kw) == status
+
+
+def test_quantize_fp8_empty_is_ok(m):
+    assert _quant(m, rows=0, X=None, q=None, sc=None) == 0
+
+
+def _lf8(m, H=A16, L=100, d=128, idx=A16, M=10, Wq=A16, ws=A16, V=50, out=A16, C=0, o=1, w=A16, wb=1 << 20):
+    return m.lib.mosaic_masked_logits_fp8(H, L, d, idx, M, Wq, ws, V, out, C, o, w, wb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), 1), (dict(V=-1), 1), (dict(L=-1), 1), (dict(d=-1), 1), (dict(o=5), 1),
+    (dict(d=64), 2), (dict(d=192), 2),                 # d % 128 != 0
+    (dict(o=0), 2),                                    # fp32 logits not offered
+    (dict(H=None), 1), (dict(idx=None), 1), (dict(Wq=None), 1), (dict(ws=None), 1), (dict(out=None), 1),
+    (dict(w=None), 1),
+    (dict(H=A8), 1), (dict(Wq=A8), 1), (dict(out=A8), 1), (dict(w=A8), 1), (dict(ws=A16 + 4), 1),
+    (dict(wb=10 * 128 + 40 - 1), 1),                   # 10 rows x 128 codes + 10 scales
+    (dict(M=1000, C=100, wb=100 * 128 + 400 - 1), 1),  # sized by the chunk
+    (dict(L=2**31), 2),
+])
+def test_logits_fp8_validation(m, kw, status):
+    assert _lf8(m, **kw) == status
+
+
+def test_logits_fp8_empty_is_ok(m):
+    assert _lf8(m, M=0, H=None, idx=None, Wq=None, ws=None, out=None, w=None, wb=0) == 0

@@ -1,0 +1,112 @@
+"""GPU FP8 (OCP E4M3) LM head vs the CPU oracle.
+
+Quantization decides integers (the codes) from fp32 arithmetic, and both sides take
+those decisions in the same fp32 operations (amax, 448 / amax, x * inv, round to
+nearest even), so codes and scales are compared bit for bit.  The logits are the fp8
+MFMA's fp32 sum of code products times both row scales, rounded to bf16; the oracle
+sums the same products exactly in fp64.  The fp8 MFMA adds its partial products with
+an error of order 1e-5 of the largest partial sum (measured), far below the bf16
+output rounding, so the bf16 bar |g - o| <= 1e-2 * max(1, |o|) applies.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mask_only_logits_amd import inputs
+from tests.helpers import assert_close, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def m():
+    from mask_only_logits_amd import mosaic
+    return mosaic
+
+
+@pytest.mark.parametrize("dtype,n,d", [("bf16", 1000, 512), ("f32", 300, 136), ("bf16", 7, 4096), ("bf16", 64, 8)])
+def test_quantize_bit_exact(m, dtype, n, d):
+    X = inputs.make_random(n + d, L=n, d=d, V=4, M=1, dtype=dtype).H.clone()
+    X[min(3, n - 1)] = 0
+    if n > 10:
+        X[5, 7] = 1e-30 if dtype == "f32" else X[5, 7]       # tiny values next to large ones
+    q, sc = m.mosaic_quantize_rows_fp8(X.to(DEV))
+    torch.cuda.synchronize()
+    oq, osc = oracle.quantize_rows_e4m3(X)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+    # gathered rows
+    ridx = np.random.default_rng(n).integers(0, n, size=min(n, 50)).astype(np.int32)
+    q2, sc2 = m.mosaic_quantize_rows_fp8(X.to(DEV), row_idx=torch.from_numpy(ridx).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(q2.cpu().numpy(), oq[ridx]) and np.array_equal(sc2.cpu().numpy(), osc[ridx])
+
+
+CASES = [
+    # (L, d, V, M, chunk_rows)
+    (700, 512, 1000, 600, 0),
+    (700, 512, 1000, 600, 256),
+    (400, 128, 1001, 257, 0),     # one K tile, V % 4 != 0
+    (400, 256, 257, 256, 0),
+    (300, 384, 3, 1, 0),          # a single row, odd K-tile count
+    (900, 3584, 700, 513, 200),
+]
+
+
+@pytest.mark.parametrize("L,d,V,M,C", CASES)
+def test_parity_random(m, L, d, V, M, C):
+    wl = inputs.make_random(L * 3 + d + V + M, L=L, d=d, V=V, M=M, dtype="bf16")
+    idx = oracle.mask_compact(wl.tokens, wl.mask_id)
+    Wq, ws = m.mosaic_quantize_rows_fp8(wl.W.to(DEV))
+    out = m.mosaic_masked_logits_fp8(wl.H.to(DEV), torch.from_numpy(idx).to(DEV), Wq, ws, chunk_rows=C)
+    torch.cuda.synchronize()
+    ref = oracle.masked_logits_fp8(wl.H, idx, wl.W)
+    assert_close(out, ref, f"fp8 {L},{d},{V},{M},{C}")
+
+
+def test_chunked_waves_and_determinism(m, monkeypatch):
+    wl = inputs.make_random(55, L=1500, d=256, V=2000, M=1100, dtype="bf16")
+    idx_d = torch.from_numpy(oracle.mask_compact(wl.tokens, wl.mask_id)).to(DEV)
+    H = wl.H.to(DEV)
+    Wq, ws = m.mosaic_quantize_rows_fp8(wl.W.to(DEV))
+    ref = m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws)
+    for C in (1, 64, 255, 256, 300, 1099, -1):
+        assert torch.equal(m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws, chunk_rows=C), ref), C
+    monkeypatch.setenv("MOSAIC_TUNE", "waves=4")
+    assert torch.equal(m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws), ref)
+    monkeypatch.delenv("MOSAIC_TUNE")
+    torch.cuda.synchronize()
+
+
+def test_close_to_bf16_logits(m):
+    wl = inputs.make_random(56, L=600, d=1024, V=3000, M=400, dtype="bf16")
+    idx = oracle.mask_compact(wl.tokens, wl.mask_id)
+    idx_d = torch.from_numpy(idx).to(DEV)
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    Wq, ws = m.mosaic_quantize_rows_fp8(W)
+    f8 = m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws).float()
+    b16 = m.mosaic_masked_logits(H, idx_d, W, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rel = ((f8 - b16).abs().max() / b16.abs().max()).item()
+    assert 1e-4 < rel < 0.05, rel
+
+
+def test_headline_shape_sampled_rows(m):
+    # LLaDA-shaped LM head (V = 126464, d = 4096) on the logits-dominant workload's
+    # masked rows, in its 4096-row chunks
+    wl = inputs.make_workload("long_logits")
+    idx = oracle.mask_compact(wl.tokens, wl.mask_id)
+    Wq, ws = m.mosaic_quantize_rows_fp8(wl.W.to(DEV))
+    out = m.mosaic_masked_logits_fp8(wl.H.to(DEV), torch.from_numpy(idx).to(DEV), Wq, ws,
+                                     chunk_rows=wl.chunk_rows)
+    torch.cuda.synchronize()
+    rows = sample_rows(idx.size, wl.chunk_rows, 4, seed=11)
+    rows = rows[np.linspace(0, rows.size - 1, 10).astype(int)]
+    qh, sh = oracle.quantize_rows_e4m3(wl.H, idx)
+    qw, sw = oracle.quantize_rows_e4m3(wl.W)
+    # the device-quantized W equals the oracle's on every code
+    assert np.array_equal(Wq.cpu().numpy(), qw) and np.array_equal(ws.cpu().numpy(), sw)
+    ref = oracle.logits_fp8(qh, sh, qw, sw, rows=rows)
+    assert_close(out[torch.from_numpy(rows).to(DEV)], ref, "fp8 long_logits sampled rows")
