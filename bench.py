@@ -52,7 +52,7 @@ def kernel_source_hash() -> str:
     a measured traffic figure stays attached to the code it was measured on."""
     import re
     h = hashlib.sha256()
-    for f in ("gather_gemm.hip", "mosaic_abi.cpp", "launch.h"):
+    for f in ("gather_gemm.hip", "gather_gemm_fp8.hip", "mosaic_abi.cpp", "launch.h"):
         with open(os.path.join(ROOT, "mask_only_logits_amd", "csrc", f), encoding="utf-8") as fh:
             text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
         for line in text.splitlines():
