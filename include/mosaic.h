@@ -103,7 +103,14 @@ mosaic_status_t mosaic_mask_compact_batched(const int32_t *tokens, int64_t L,
  *   H      [L, d] row-major, in_dtype   final hidden states of ALL L positions.
  *   idx    int32[M]                     rows of H to use, each in [0, L); any order,
  *                                       repeats allowed.  Out-of-range values are a
- *                                       contract violation (undefined behaviour).
+ *                                       contract violation (undefined behaviour), unless
+ *                                       the environment has MOSAIC_CHECK_IDX=1: then
+ *                                       every logits entry point first checks idx on the
+ *                                       device, waits for the answer (synchronous) and
+ *                                       returns INVALID_ARG, enqueuing no compute and
+ *                                       touching no output, if a value is out of range
+ *                                       (a debug mode; it allocates a 4-byte flag once
+ *                                       per device).
  *   W      [V, d] row-major, in_dtype   LM-head weight (K-contiguous rows).
  *   out    [M, V] row-major, out_dtype  row i holds the logits of position idx[i].
  *   chunk_rows  max_num_logits: <= 0 or >= M runs one chunk; otherwise

@@ -18,6 +18,8 @@
 // a single workgroup finishes in a few microseconds, so no cross-workgroup scan
 // (and no workspace) is needed.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "launch.h"
@@ -110,7 +112,36 @@ __global__ __launch_bounds__(256) void csr_offsets_kernel(const int32_t *__restr
     idx_offsets[s] = lo;
 }
 
+// Index-list check (debug mode of the logits entry points): flag[0] is set to 1 when
+// some idx[i], i < M, lies outside [0, L).  Only the lanes that find a bad index store,
+// all the same value, so no atomic is needed.
+__global__ __launch_bounds__(256) void idx_range_check_kernel(const int32_t *__restrict__ idx, int64_t M,
+                                                              int64_t L, int32_t *__restrict__ flag)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < M; i += (int64_t)gridDim.x * 256) {
+        const int32_t v = idx[i];
+        if (v < 0 || (int64_t)v >= L)
+            flag[0] = 1;
+    }
+}
+
+__global__ void flag_clear_kernel(int32_t *__restrict__ flag)
+{
+    if (threadIdx.x == 0)
+        flag[0] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_idx_range_check(const int32_t *idx, int64_t M, int64_t L, int32_t *flag, hipStream_t stream)
+{
+    hipLaunchKernelGGL(flag_clear_kernel, dim3(1), dim3(64), 0, stream, flag);
+    if (M > 0) {
+        const int64_t blocks = std::min<int64_t>((M + 255) / 256, 1024);
+        hipLaunchKernelGGL(idx_range_check_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, idx, M, L, flag);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_mask_compact(const int32_t *tokens, int64_t L, int32_t mask_id, int32_t *idx,
                                int32_t *count, hipStream_t stream)

@@ -304,36 +304,88 @@ gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__
     }
 
     // epilogue: lane holds vocabulary entries v0 + wv*WV + 32a + 8gq + 4hi + (0..3) of
-    // masked row m0 + wm*WM + 32bm + fr
-    const bool vec_ok = ((uintptr_t)out & 7) == 0 && (ldo & 3) == 0;
+    // masked row m0 + wm*WM + 32bm + fr.  Four waves (256 accumulators, registers to
+    // spare): after scaling and rounding, permlane32_swap gives lanes 0-31 entries 0-7 /
+    // 16-23 of a 32-entry block and lanes 32-63 entries 8-15 / 24-31, and every lane
+    // stores 16 bytes.  Eight waves: the swap's extra registers spill, so each lane
+    // stores its 4 entries (8 bytes) directly (measured faster for each wave count).
+    auto pack2 = [](float x, float y) {
+        const __bf16 a = static_cast<__bf16>(x), b = static_cast<__bf16>(y);
+        return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    };
+    if constexpr (NW == 4) {
+        const bool vec_ok = ((uintptr_t)out & 15) == 0 && (ldo & 7) == 0;
 #pragma unroll
-    for (int bm = 0; bm < AM; ++bm) {
-        const int row = m0 + wm * WM + bm * 32 + fr;
-        if (row >= rows)
-            continue;
-        const float h = hs[row];
+        for (int bm = 0; bm < AM; ++bm) {
+            const int row = m0 + wm * WM + bm * 32 + fr;
+            const bool row_ok = row < rows;
+            const float h = hs[min(row, rows - 1)];
 #pragma unroll
-        for (int a = 0; a < AV; ++a) {
+            for (int a = 0; a < AV; ++a) {
+                const int vb = v0 + wv * WV + a * 32;
+                uint32_t pk[4][2];
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int v = v0 + wv * WV + a * 32 + gq * 8 + hi * 4;
-                __bf16 *o = out + (int64_t)row * ldo + v;
-                if (vec_ok && v + 3 < V) {
-                    const f32x4_t w = *(const f32x4_t *)(ws + v);
-                    uint32_t p[2];
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int v = vb + gq * 8 + hi * 4;
+                    float w[4];
+                    if (v + 3 < V) {
+                        const f32x4_t w4 = *(const f32x4_t *)(ws + v);
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const __bf16 lo = static_cast<__bf16>(acc[a][bm][gq * 4 + 2 * e] * (h * w[2 * e]));
-                        const __bf16 up = static_cast<__bf16>(acc[a][bm][gq * 4 + 2 * e + 1] * (h * w[2 * e + 1]));
-                        p[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                               ((uint32_t)__builtin_bit_cast(uint16_t, up) << 16);
+                        for (int e = 0; e < 4; ++e)
+                            w[e] = w4[e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            w[e] = ws[min(v + e, V - 1)];
                     }
-                    *(uint2 *)o = make_uint2(p[0], p[1]);
-                } else {
+                    pk[gq][0] = pack2(acc[a][bm][gq * 4 + 0] * (h * w[0]), acc[a][bm][gq * 4 + 1] * (h * w[1]));
+                    pk[gq][1] = pack2(acc[a][bm][gq * 4 + 2] * (h * w[2]), acc[a][bm][gq * 4 + 3] * (h * w[3]));
+                }
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (v + e < V)
-                            o[e] = static_cast<__bf16>(acc[a][bm][gq * 4 + e] * (h * ws[v + e]));
+                for (int pr = 0; pr < 2; ++pr) {
+                    const auto s0 = __builtin_amdgcn_permlane32_swap(pk[2 * pr][0], pk[2 * pr + 1][0], false, false);
+                    const auto s1 = __builtin_amdgcn_permlane32_swap(pk[2 * pr][1], pk[2 * pr + 1][1], false, false);
+                    const int v = vb + 16 * pr + 8 * hi;
+                    if (!row_ok)
+                        continue;   // (after the swaps: every lane takes part in them)
+                    __bf16 *o = out + (int64_t)row * ldo + v;
+                    if (vec_ok && v + 7 < V) {
+                        *(uint4 *)o = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+                    } else {
+                        const uint32_t w4[4] = {s0[0], s1[0], s0[1], s1[1]};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (v + e < V)
+                                o[e] = __builtin_bit_cast(__bf16, (uint16_t)(w4[e >> 1] >> (16 * (e & 1))));
+                    }
+                }
+            }
+        }
+    } else {
+        const bool vec_ok = ((uintptr_t)out & 7) == 0 && (ldo & 3) == 0;
+#pragma unroll
+        for (int bm = 0; bm < AM; ++bm) {
+            const int row = m0 + wm * WM + bm * 32 + fr;
+            if (row >= rows)
+                continue;
+            const float h = hs[row];
+#pragma unroll
+            for (int a = 0; a < AV; ++a) {
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int v = v0 + wv * WV + a * 32 + gq * 8 + hi * 4;
+                    __bf16 *o = out + (int64_t)row * ldo + v;
+                    if (vec_ok && v + 3 < V) {
+                        const f32x4_t w = *(const f32x4_t *)(ws + v);
+                        *(uint2 *)o = make_uint2(
+                            pack2(acc[a][bm][gq * 4 + 0] * (h * w[0]), acc[a][bm][gq * 4 + 1] * (h * w[1])),
+                            pack2(acc[a][bm][gq * 4 + 2] * (h * w[2]), acc[a][bm][gq * 4 + 3] * (h * w[3])));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (v + e < V)
+                                o[e] = static_cast<__bf16>(acc[a][bm][gq * 4 + e] * (h * ws[v + e]));
+                    }
                 }
             }
         }

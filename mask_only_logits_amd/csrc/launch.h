@@ -5,6 +5,9 @@
 
 namespace mosaic {
 
+// flag[0] = 1 if some idx[i] (i < M) is outside [0, L), else 0 (clears flag first).
+hipError_t launch_idx_range_check(const int32_t *idx, int64_t M, int64_t L, int32_t *flag, hipStream_t stream);
+
 hipError_t launch_mask_compact(const int32_t *tokens, int64_t L, int32_t mask_id, int32_t *idx,
                                int32_t *count, hipStream_t stream);
 hipError_t launch_mask_compact_flags(const uint8_t *flags, int64_t L, int32_t *idx, int32_t *count,

@@ -14,6 +14,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
+
 #include "../../include/mosaic.h"
 #include "launch.h"
 
@@ -61,6 +64,40 @@ Tune read_tune()
     if ((p = strstr(e, "waves=")) && atoi(p + 6) == 4)
         t.waves = 4;
     return t;
+}
+
+// Debug mode MOSAIC_CHECK_IDX=1: before any compute is enqueued, check on the device
+// that every idx[i] (i < M) lies in [0, L), and wait for the answer.  A 4-byte device
+// flag is allocated once per device on first use.  Returns MOSAIC_OK (mode off, or all
+// indices valid), MOSAIC_ERR_INVALID_ARG (an index out of range) or MOSAIC_ERR_DEVICE.
+mosaic_status_t check_idx_if_asked(const int32_t *idx, int64_t M, int64_t L, hipStream_t stream)
+{
+    const char *e = getenv("MOSAIC_CHECK_IDX");
+    if (!e || e[0] != '1')
+        return MOSAIC_OK;
+    static std::mutex mu;
+    static std::map<int, int32_t *> flags;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return MOSAIC_ERR_DEVICE;
+    int32_t *flag = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        auto it = flags.find(dev);
+        if (it == flags.end()) {
+            if (hipMalloc((void **)&flag, sizeof(int32_t)) != hipSuccess)
+                return MOSAIC_ERR_DEVICE;
+            flags[dev] = flag;
+        } else {
+            flag = it->second;
+        }
+    }
+    int32_t host = 0;
+    if (mosaic::launch_idx_range_check(idx, M, L, flag, stream) != hipSuccess ||
+        hipMemcpyAsync(&host, flag, sizeof host, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return MOSAIC_ERR_DEVICE;
+    return host ? MOSAIC_ERR_INVALID_ARG : MOSAIC_OK;
 }
 
 bool variant_can_run(int v, int64_t M, int64_t d, mosaic_dtype_t in, mosaic_dtype_t out)
@@ -227,6 +264,9 @@ mosaic_status_t mosaic_masked_logits(const void *H, int64_t L, int64_t d, const 
     if (v_full < 0 || v_tail < 0 || !mosaic::gather_gemm_grid_fits(v_full, C, V) ||
         !mosaic::gather_gemm_grid_fits(v_tail, tail, V))
         return MOSAIC_ERR_UNSUPPORTED;
+    const mosaic_status_t ck = check_idx_if_asked(idx, M, L, (hipStream_t)stream);
+    if (ck != MOSAIC_OK)
+        return ck;
     const bool out_bf16 = out_dtype == MOSAIC_BF16;
     const int group_m = read_tune().group_m;
     for (int64_t k = 0; k < K; ++k) {
@@ -319,6 +359,9 @@ mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_
     float *pmax = (float *)workspace;
     int32_t *parg = (int32_t *)(pmax + plane);
     float *psum = (float *)(parg + plane);
+    const mosaic_status_t ck = check_idx_if_asked(idx, M, L, (hipStream_t)stream);
+    if (ck != MOSAIC_OK)
+        return ck;
     const int group_m = read_tune().group_m;
     for (int64_t k = 0; k < K; ++k) {
         const int64_t r0 = k * C;
@@ -398,6 +441,9 @@ mosaic_status_t mosaic_masked_logits_fp8(const void *H, int64_t L, int64_t d, co
     // workspace: the chunk's codes [C, d], then its row scales [C]
     uint8_t *hq = (uint8_t *)workspace;
     float *hs = (float *)(hq + (C * d + 15) / 16 * 16);
+    const mosaic_status_t ck = check_idx_if_asked(idx, M, L, (hipStream_t)stream);
+    if (ck != MOSAIC_OK)
+        return ck;
     const Tune t = read_tune();
     for (int64_t k = 0; k < K; ++k) {
         const int64_t r0 = k * C;
