@@ -29,6 +29,7 @@ namespace mosaic {
 namespace {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -212,10 +213,12 @@ gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__
     const int lane_chunk = ((2 * hi) ^ swz(fr)) * 16;
     const int a_addr = (wv * WV + fr) * ROW_BYTES + lane_chunk;
     const int b_addr = W_TILE + (wm * WM + fr) * ROW_BYTES + lane_chunk;
+    // (native vector loads: the compiler keeps their type-based alias information and so
+    // does not wait for the stage DMA before each read; HIP's uint4 struct loads lose it)
     auto frag = [&](int addr, int s) {
-        const uint4 lo = *(const uint4 *)(smem + (addr ^ (64 * s)));
-        const uint4 up = *(const uint4 *)(smem + (addr ^ (64 * s + 16)));
-        return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)up.x, (int)up.y, (int)up.z, (int)up.w};
+        const i32x4_t lo = *(const i32x4_t *)(smem + (addr ^ (64 * s)));
+        const i32x4_t up = *(const i32x4_t *)(smem + (addr ^ (64 * s + 16)));
+        return i32x8_t{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
     };
     auto load_frags = [&](int so, int s, i32x8_t (&af)[AV], i32x8_t (&bf)[AM]) {
 #pragma unroll

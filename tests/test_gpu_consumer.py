@@ -168,3 +168,19 @@ def test_headline_shape_sampled_rows(m):
     torch.cuda.synchronize()
     for x, y in zip(got[:3], again[:3]):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("name", ["ragged", "lowm", "llada_step"])
+def test_other_workloads_sampled_rows(m, name):
+    # Dream-shaped (d = 3584, V = 152064) ragged batch and low-M case, and the LLaDA step
+    wl = inputs.make_workload(name)
+    if wl.seq_offsets is not None:
+        idx = oracle.mask_compact_batched(wl.tokens, wl.seq_offsets, wl.mask_id)[0]
+    else:
+        idx = oracle.mask_compact(wl.tokens, wl.mask_id)
+    idx_d = torch.from_numpy(idx).to(DEV)
+    got = m.mosaic_masked_logits_argmax_lse(wl.H.to(DEV), idx_d, wl.W.to(DEV), chunk_rows=wl.chunk_rows)
+    torch.cuda.synchronize()
+    rows = sample_rows(idx.size, wl.chunk_rows, 4, seed=3)
+    rows = rows[np.linspace(0, rows.size - 1, min(rows.size, 10)).astype(int)]
+    _check(got, wl.H, idx, wl.W, rows=rows, what=name)

@@ -74,8 +74,10 @@ def test_chunked_waves_and_determinism(m, monkeypatch):
     ref = m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws)
     for C in (1, 64, 255, 256, 300, 1099, -1):
         assert torch.equal(m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws, chunk_rows=C), ref), C
-    monkeypatch.setenv("MOSAIC_TUNE", "waves=4")
-    assert torch.equal(m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws), ref)
+    for tune in ("waves=8",):
+        monkeypatch.setenv("MOSAIC_TUNE", tune)
+        assert torch.equal(m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws), ref), tune
+        assert torch.equal(m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws, chunk_rows=300), ref), tune
     monkeypatch.delenv("MOSAIC_TUNE")
     torch.cuda.synchronize()
 
@@ -110,3 +112,13 @@ def test_headline_shape_sampled_rows(m):
     assert np.array_equal(Wq.cpu().numpy(), qw) and np.array_equal(ws.cpu().numpy(), sw)
     ref = oracle.logits_fp8(qh, sh, qw, sw, rows=rows)
     assert_close(out[torch.from_numpy(rows).to(DEV)], ref, "fp8 long_logits sampled rows")
+
+
+def test_dream_shape_low_m_all_rows(m):
+    # the low-M workload (Dream-shaped LM head: d = 3584, V = 152064; M = 20), every row
+    wl = inputs.make_workload("lowm")
+    idx = oracle.mask_compact(wl.tokens, wl.mask_id)
+    Wq, ws = m.mosaic_quantize_rows_fp8(wl.W.to(DEV))
+    out = m.mosaic_masked_logits_fp8(wl.H.to(DEV), torch.from_numpy(idx).to(DEV), Wq, ws)
+    torch.cuda.synchronize()
+    assert_close(out, oracle.masked_logits_fp8(wl.H, idx, wl.W), "fp8 lowm")
