@@ -349,7 +349,8 @@ def main():
     kernel = "gather_gemm_fp8_kernel" if fp8 else "gather_gemm_bf16_defer_kernel" if consumer else {0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel", 6: "gather_gemm_lowm_kernel",
               9: "gather_gemm_bf16_persist_kernel", 10: "gather_gemm_bf16_persist_kernel",
               11: "gather_gemm_bf16_persist_kernel", 15: "gather_gemm_bf16_defer_kernel",
-              16: "gather_gemm_bf16_defer_kernel", 17: "gather_gemm_bf16_defer_kernel"}.get(variant, "gather_gemm_bf16_kernel")
+              16: "gather_gemm_bf16_defer_kernel", 17: "gather_gemm_bf16_defer_kernel",
+              18: "gather_gemm_bf16_defer_kernel", 19: "gather_gemm_bf16_defer_kernel"}.get(variant, "gather_gemm_bf16_kernel")
     if variant == 6:
         # streaming W is the bound: algorithmic bytes per launch over the launch time
         achieved_gbs = alg_bytes / launches / (gemm_avg / launches / 1e3) / 1e9

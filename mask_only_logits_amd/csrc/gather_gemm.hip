@@ -40,6 +40,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 
 #include "launch.h"
@@ -724,7 +725,17 @@ gather_gemm_bf16_persist_kernel(const __bf16 *__restrict__ H, const int32_t *__r
 // (row, vocabulary tile) goes to pmax / parg / psum ([nvt][rows], column-major so a
 // wave's 32 rows are consecutive words); mosaic_logits_reduce_finish combines them.
 // STORE = false skips the logits stores (consumer-only use: the logits never exist).
-template <int NSPREAD, int DEFER, int NIMM, bool STORE = true, bool REDUCE = false>
+//
+// M16: the same tile with v_mfma_f32_16x16x32_bf16 (a wave's 128 x 64 as 8 x 4 blocks of
+// 16 x 16, k 32 per instruction, so one K tile is two k sub-steps instead of four).  The
+// same k order gives results bit-identical to the 32 x 32 x 16 form (measured), and it
+// runs about 4% faster.  A sub-step's fragments take twice the registers, which leaves
+// no room for deferred stores (they push the K loop into spilling: measured slower, also
+// with the deferred words parked in LDS), so the M16 forms store each tile at its end.
+// A lane holds four consecutive vocabulary entries of one row per block; permlane16_swap
+// pairs the lanes of neighbouring blocks into 16-byte stores, and the four lanes of a row
+// combine their consumer partials through permlane16_swap and permlane32_swap.
+template <int NSPREAD, int DEFER, int NIMM, bool STORE = true, bool REDUCE = false, bool M16 = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
 gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict__ idx, int32_t rows,
                               const __bf16 *__restrict__ W, int32_t V, int32_t d, __bf16 *__restrict__ out,
@@ -739,12 +750,17 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     constexpr int H_TILE = BM * ROW_BYTES;
     constexpr int STAGE = W_TILE + H_TILE;
     constexpr int WV = BV / 2, WM = BM / (NW / 2);
-    constexpr int AV = WV / 32, AM = WM / 32;
+    constexpr int MB = M16 ? 16 : 32;         // MFMA block edge
+    constexpr int KI = M16 ? 32 : 16;         // k per MFMA
+    constexpr int NACC = MB * MB / 64;        // accumulators per lane and block
+    constexpr int AV = WV / MB, AM = WM / MB;
     constexpr int LW = BV / RPI / NW, LH = BM / RPI / NW;
-    constexpr int NSUB = BK / 16;
+    constexpr int NSUB = BK / KI;
     constexpr int NDMA = LW + LH;
     constexpr int NFR = AV + AM;
-    constexpr int NST = AV * AM * 2;          // 16-byte stores per lane and tile
+    constexpr int NST = M16 ? AV * AM / 2 : AV * AM * 2;   // 16-byte stores per lane and tile
+    constexpr int HOOK_S = NSUB > 2 ? 1 : 0;  // k sub-step that issues a step's deferred stores
+    using acc_t = typename std::conditional<M16, f32x4_t, f32x16_t>::type;
     static_assert(NSPREAD >= 1 && NSPREAD <= NSUB && NDMA % NSPREAD == 0, "spread");
     static_assert(NIMM >= 0 && NIMM <= NST && DEFER >= 1 && (NST - NIMM) % DEFER == 0, "defer");
     constexpr int PER = NDMA / NSPREAD;
@@ -839,36 +855,75 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
         }
     };
 
-    f32x16_t acc[AV][AM];
-#pragma unroll
-    for (int a = 0; a < AV; ++a)
-#pragma unroll
-        for (int bm = 0; bm < AM; ++bm)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[a][bm][e] = 0.0f;
-
-    const int fr = lane & 31, hi = lane >> 5;
-    const int lane_chunk = (hi ^ swz<BK>(fr)) * 16;
-    const int a_addr = (wv * WV + fr) * ROW_BYTES + lane_chunk;
-    const int b_addr = W_TILE + (wm * WM + fr) * ROW_BYTES + lane_chunk;
-
-    auto load_frags = [&](int so, int s, bf16x8_t (&af)[AV], bf16x8_t (&bf)[AM]) {
-        const int ab = (a_addr + so) ^ (32 * s), bb = (b_addr + so) ^ (32 * s);
-#pragma unroll
-        for (int a = 0; a < AV; ++a)
-            af[a] = *(const bf16x8_t *)(smem + ab + a * 32 * ROW_BYTES);
-#pragma unroll
-        for (int bm = 0; bm < AM; ++bm)
-            bf[bm] = *(const bf16x8_t *)(smem + bb + bm * 32 * ROW_BYTES);
-    };
-    auto mma = [&](const bf16x8_t (&af)[AV], const bf16x8_t (&bf)[AM]) {
+    acc_t acc[AV][AM];
+    auto zero_acc = [&]() {
 #pragma unroll
         for (int a = 0; a < AV; ++a)
 #pragma unroll
             for (int bm = 0; bm < AM; ++bm)
-                acc[a][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bf[bm], acc[a][bm], 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < NACC; ++e)
+                    acc[a][bm][e] = 0.0f;
     };
+    zero_acc();
+
+    // Fragment lanes.  32 x 32 x 16: lane l reads block row l % 32, k chunk 2s + l / 32 of
+    // sub-step s.  16 x 16 x 32: lane l reads block row l % 16, k chunk 4s + l / 16.  The
+    // swizzle of a row depends on the lane only (blocks start at multiples of 16 rows), and
+    // a sub-step's chunk bits sit above the lane's, so sub-step s is an XOR of the address.
+    const int fr = lane & 31, hi = lane >> 5;     // 32 x 32 lanes
+    const int r16 = lane & 15, qd = lane >> 4;    // 16 x 16 lanes
+    const int lane_row = M16 ? r16 : fr;
+    const int lane_chunk = ((M16 ? qd : hi) ^ swz<BK>(lane_row)) * 16;
+    const int a_addr = (wv * WV + lane_row) * ROW_BYTES + lane_chunk;
+    const int b_addr = W_TILE + (wm * WM + lane_row) * ROW_BYTES + lane_chunk;
+    constexpr int SUB_BYTES = KI * 2;
+
+    auto load_frags = [&](int so, int s, bf16x8_t (&af)[AV], bf16x8_t (&bf)[AM]) __attribute__((always_inline)) {
+        const int ab = (a_addr + so) ^ (SUB_BYTES * s), bb = (b_addr + so) ^ (SUB_BYTES * s);
+#pragma unroll
+        for (int a = 0; a < AV; ++a)
+            af[a] = *(const bf16x8_t *)(smem + ab + a * MB * ROW_BYTES);
+#pragma unroll
+        for (int bm = 0; bm < AM; ++bm)
+            bf[bm] = *(const bf16x8_t *)(smem + bb + bm * MB * ROW_BYTES);
+    };
+    auto mma = [&](const bf16x8_t (&af)[AV], const bf16x8_t (&bf)[AM]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int a = 0; a < AV; ++a)
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm) {
+                if constexpr (M16)
+                    acc[a][bm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bf[bm], acc[a][bm], 0, 0, 0);
+                else
+                    acc[a][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bf[bm], acc[a][bm], 0, 0, 0);
+            }
+    };
+    // MFMAs on fragment buffer `cur` while the fragments of k sub-step s of stage so are read.
+    // 32 x 32: both operands double-buffered.  16 x 16 (twice the fragment registers per
+    // sub-step): the B fragments are double-buffered, the A fragments single: block a's
+    // next fragment is read right after the last MFMA of its row.
+    auto mma_load = [&](int so, int s, int cur, bf16x8_t (&af)[2][AV], bf16x8_t (&bf)[2][AM]) __attribute__((always_inline)) {
+        if constexpr (M16) {
+            const int ab = (a_addr + so) ^ (SUB_BYTES * s), bb = (b_addr + so) ^ (SUB_BYTES * s);
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm)
+                bf[cur ^ 1][bm] = *(const bf16x8_t *)(smem + bb + bm * MB * ROW_BYTES);
+#pragma unroll
+            for (int a = 0; a < AV; ++a) {
+#pragma unroll
+                for (int bm = 0; bm < AM; ++bm)
+                    acc[a][bm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][a], bf[cur][bm], acc[a][bm], 0, 0, 0);
+                af[0][a] = *(const bf16x8_t *)(smem + ab + a * MB * ROW_BYTES);
+            }
+        } else {
+            load_frags(so, s, af[cur ^ 1], bf[cur ^ 1]);
+            mma(af[cur], bf[cur]);
+        }
+    };
+    // Instruction order of one k sub-step: each refill DMA issue beside an MFMA, then the
+    // fragment reads spread over the MFMAs (16 x 16: the B reads first, then each A read
+    // after its row's MFMAs).
     auto interleave = [&](int nvm) {
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) {
@@ -877,23 +932,50 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
         }
+        if constexpr (M16) {
 #pragma unroll
-        for (int i = 0; i < NFR; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int bm = 0; bm < AM; ++bm) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            const int used = nvm + AM;
+#pragma unroll
+            for (int a = 0; a < AV; ++a) {
+#pragma unroll
+                for (int c = 0; c < AM; ++c)
+                    if (a * AM + c >= used)
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NFR; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
         }
     };
 
-    // ---- results of the previous tile, as 16-byte store words: store j covers block
+    // ---- results of the previous tile, as 16-byte store words.  32 x 32: store j covers block
     // (a, bm) = ((j / 2) / AM, (j / 2) % AM), vocabulary entries 16 * (j % 2) + 8 * hi + (0..7)
-    // of that block for masked row 32 * bm + fr of the wave's sub-tile.
+    // of that block for masked row 32 * bm + fr of the wave's sub-tile.  16 x 16: store j
+    // covers the block pair (2 * (j / AM), +1) of row block bm = j % AM; a lane with even qd
+    // holds entries 4 * qd + (0..7) of the first block, one with odd qd entries
+    // 4 * (qd - 1) + (0..7) of the second, for masked row 16 * bm + r16.
     uint32_t pk[NST][4];
     int pm0 = 0, pv0 = 0;
     const bool vec_ok = ((uintptr_t)out & 15) == 0 && (ldo & 7) == 0;
     auto store_one = [&](int j) {
-        const int a = (j >> 1) / AM, bm = (j >> 1) % AM, pr = j & 1;
-        const int row = pm0 + wm * WM + bm * 32 + fr;
-        const int v = pv0 + wv * WV + a * 32 + 16 * pr + 8 * hi;
+        int row, v;
+        if constexpr (M16) {
+            const int ap = j / AM, bm = j % AM;
+            row = pm0 + wm * WM + bm * 16 + r16;
+            v = pv0 + wv * WV + (2 * ap + (qd & 1)) * 16 + 4 * (qd & 2);
+        } else {
+            const int a = (j >> 1) / AM, bm = (j >> 1) % AM, pr = j & 1;
+            row = pm0 + wm * WM + bm * 32 + fr;
+            v = pv0 + wv * WV + a * 32 + 16 * pr + 8 * hi;
+        }
         if (row < rows) {
             __bf16 *o = out + (int64_t)row * ldo + v;
             if (vec_ok && v + 7 < V) {
@@ -906,9 +988,28 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
             }
         }
     };
-    // acc -> pk (round to bf16; lanes 0-31 take entries 0-7 / 16-23 of a block, lanes 32-63
-    // entries 8-15 / 24-31), then restart the accumulators
+    // acc -> pk (round to bf16; 32 x 32: lanes 0-31 take entries 0-7 / 16-23 of a block,
+    // lanes 32-63 entries 8-15 / 24-31; 16 x 16: permlane16_swap trades the odd-qd lanes'
+    // words of the first block of a pair for the even-qd lanes' words of the second), then
+    // restart the accumulators
     auto pack = [&]() {
+        if constexpr (M16) {
+#pragma unroll
+            for (int ap = 0; ap < AV / 2; ++ap)
+#pragma unroll
+                for (int bm = 0; bm < AM; ++bm) {
+                    const auto &x = acc[2 * ap][bm], &y = acc[2 * ap + 1][bm];
+                    const auto s0 = __builtin_amdgcn_permlane16_swap(pack_bf16x2(x[0], x[1]), pack_bf16x2(y[0], y[1]),
+                                                                     false, false);
+                    const auto s1 = __builtin_amdgcn_permlane16_swap(pack_bf16x2(x[2], x[3]), pack_bf16x2(y[2], y[3]),
+                                                                     false, false);
+                    const int j = ap * AM + bm;
+                    pk[j][0] = s0[0];
+                    pk[j][1] = s1[0];
+                    pk[j][2] = s0[1];
+                    pk[j][3] = s1[1];
+                }
+        } else {
 #pragma unroll
         for (int a = 0; a < AV; ++a)
 #pragma unroll
@@ -929,10 +1030,9 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
                     pk[j][2] = s0[1];
                     pk[j][3] = s1[1];
                 }
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    acc[a][bm][e] = 0.0f;
             }
+        }
+        zero_acc();
     };
 
     // ---- per-row consumer partials of the current tile (REDUCE)
@@ -951,49 +1051,65 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     };
     float rm[AM], rs[AM];
     int ra[AM];
-    // lane-pair partials of rows 32 * bm + fr of the wave's sub-tile; then the upper
-    // vocabulary half's waves leave theirs in LDS
+    // Per-lane partials of every row of the wave's sub-tile (entries in ascending
+    // vocabulary order), combined over the lanes that share the row (32 x 32: the two lanes
+    // l and l ^ 32; 16 x 16: the four lanes l ^ 16, l ^ 32); then the upper vocabulary
+    // half's waves leave theirs in LDS.
+    const int row_lane = M16 ? r16 : fr;
+    const bool row_owner = M16 ? qd == 0 : hi == 0;
     auto reduce_part1 = [&](int v0) {
 #pragma unroll
         for (int bm = 0; bm < AM; ++bm) {
             float m = -INFINITY, sm = 0.0f;
             int am = INT32_MAX;
+            // entry e of this lane's block a, in ascending vocabulary order
+            auto ventry = [&](int a, int e) {
+                return M16 ? v0 + wv * WV + a * 16 + 4 * qd + e
+                           : v0 + wv * WV + a * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
+            };
 #pragma unroll
             for (int a = 0; a < AV; ++a)
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int v = v0 + wv * WV + a * 32 + gq * 8 + hi * 4 + j;
-                        const float x = acc[a][bm][gq * 4 + j];
-                        if (v < V && x > m) {
-                            m = x;
-                            am = v;
-                        }
+                for (int e = 0; e < NACC; ++e) {
+                    const float x = acc[a][bm][e];
+                    if (ventry(a, e) < V && x > m) {
+                        m = x;
+                        am = ventry(a, e);
                     }
+                }
 #pragma unroll
             for (int a = 0; a < AV; ++a)
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int v = v0 + wv * WV + a * 32 + gq * 8 + hi * 4 + j;
-                        if (v < V)
-                            sm += __builtin_amdgcn_exp2f((acc[a][bm][gq * 4 + j] - m) * kLog2e);
-                    }
-            // the partner lane (same row, the other four entries of every group of 8)
-            const auto pm = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, m),
-                                                             __builtin_bit_cast(uint32_t, m), false, false);
-            const auto pa = __builtin_amdgcn_permlane32_swap((uint32_t)am, (uint32_t)am, false, false);
-            const auto ps = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, sm),
-                                                             __builtin_bit_cast(uint32_t, sm), false, false);
-            combine(m, am, sm, __builtin_bit_cast(float, hi ? pm[0] : pm[1]), (int)(hi ? pa[0] : pa[1]),
-                    __builtin_bit_cast(float, hi ? ps[0] : ps[1]));
+                for (int e = 0; e < NACC; ++e)
+                    if (ventry(a, e) < V)
+                        sm += __builtin_amdgcn_exp2f((acc[a][bm][e] - m) * kLog2e);
+            // partner lanes: permlaneN_swap(x, x) gives the upper lane of each pair the
+            // lower one's x in [0] and the lower lane the upper one's in [1]
+            auto fold_swap32 = [&]() {
+                const auto pm = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, m),
+                                                                 __builtin_bit_cast(uint32_t, m), false, false);
+                const auto pa = __builtin_amdgcn_permlane32_swap((uint32_t)am, (uint32_t)am, false, false);
+                const auto ps = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, sm),
+                                                                 __builtin_bit_cast(uint32_t, sm), false, false);
+                combine(m, am, sm, __builtin_bit_cast(float, hi ? pm[0] : pm[1]), (int)(hi ? pa[0] : pa[1]),
+                        __builtin_bit_cast(float, hi ? ps[0] : ps[1]));
+            };
+            if constexpr (M16) {
+                const bool up = qd & 1;
+                const auto pm = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, m),
+                                                                 __builtin_bit_cast(uint32_t, m), false, false);
+                const auto pa = __builtin_amdgcn_permlane16_swap((uint32_t)am, (uint32_t)am, false, false);
+                const auto ps = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, sm),
+                                                                 __builtin_bit_cast(uint32_t, sm), false, false);
+                combine(m, am, sm, __builtin_bit_cast(float, up ? pm[0] : pm[1]), (int)(up ? pa[0] : pa[1]),
+                        __builtin_bit_cast(float, up ? ps[0] : ps[1]));
+            }
+            fold_swap32();
             rm[bm] = m;
             ra[bm] = am;
             rs[bm] = sm;
-            if (wv == 1 && hi == 0) {
-                const int r = wm * WM + bm * 32 + fr;
+            if (wv == 1 && row_owner) {
+                const int r = wm * WM + bm * MB + row_lane;
                 red_lds[r] = m;
                 red_lds[BM + r] = __builtin_bit_cast(float, am);
                 red_lds[2 * BM + r] = sm;
@@ -1002,12 +1118,12 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     };
     // after a barrier: the lower half's waves add the upper half and write the partial
     auto reduce_part2 = [&](int m0, int v0) {
-        if (wv != 0 || hi != 0)
+        if (wv != 0 || !row_owner)
             return;
         const int64_t col = (int64_t)(v0 / BV) * rows;
 #pragma unroll
         for (int bm = 0; bm < AM; ++bm) {
-            const int r = wm * WM + bm * 32 + fr;
+            const int r = wm * WM + bm * MB + row_lane;
             float m = rm[bm], sm = rs[bm];
             int am = ra[bm];
             combine(m, am, sm, red_lds[r], __builtin_bit_cast(int, red_lds[BM + r]), red_lds[2 * BM + r]);
@@ -1043,10 +1159,9 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
             for (int s = 0; s + 1 < NSUB; ++s) {
                 if (s + 1 < NSPREAD && pending)
                     issue_part(pso, pkt, s + 1);
-                if (s == 1)
+                if (s == HOOK_S)
                     hook();
-                load_frags(rd, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
-                mma(af[s & 1], bf[s & 1]);
+                mma_load(rd, s + 1, s & 1, af, bf);
                 interleave(s + 1 < NSPREAD ? PER : 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -1058,8 +1173,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
             pkt = kt + NSTAGE;
             pending = NSPREAD > 1;
             const int nx = (rd + STAGE == NSTAGE * STAGE) ? 0 : rd + STAGE;
-            load_frags(nx, 0, af[NSUB & 1], bf[NSUB & 1]);
-            mma(af[(NSUB - 1) & 1], bf[(NSUB - 1) & 1]);
+            mma_load(nx, 0, (NSUB - 1) & 1, af, bf);
             interleave(PER);
             __builtin_amdgcn_sched_barrier(0);
             rd = nx;
@@ -1087,17 +1201,27 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
             for (int s = 0; s + 1 < NSUB; ++s) {
                 if (s + 1 < NSPREAD && pending)
                     issue_part(pso, pkt, s + 1);
-                load_frags(rd, s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
-                mma(af[s & 1], bf[s & 1]);
+                mma_load(rd, s + 1, s & 1, af, bf);
             }
             pending = false;
-            if (kt + 1 < nk) {
-                wait_vmcnt<0>();
-                barrier_no_fence();
-                rd = (rd + STAGE == NSTAGE * STAGE) ? 0 : rd + STAGE;
-                load_frags(rd, 0, af[NSUB & 1], bf[NSUB & 1]);
+            if constexpr (M16) {
+                // one MFMA sequence for both cases (two copies of it raise the register
+                // pressure); after the last K tile its fragment reads are unused
+                if (kt + 1 < nk) {
+                    wait_vmcnt<0>();
+                    barrier_no_fence();
+                    rd = (rd + STAGE == NSTAGE * STAGE) ? 0 : rd + STAGE;
+                }
+                mma_load(rd, 0, (NSUB - 1) & 1, af, bf);
+            } else {
+                if (kt + 1 < nk) {
+                    wait_vmcnt<0>();
+                    barrier_no_fence();
+                    rd = (rd + STAGE == NSTAGE * STAGE) ? 0 : rd + STAGE;
+                    load_frags(rd, 0, af[NSUB & 1], bf[NSUB & 1]);
+                }
+                mma(af[(NSUB - 1) & 1], bf[(NSUB - 1) & 1]);
             }
-            mma(af[(NSUB - 1) & 1], bf[(NSUB - 1) & 1]);
         }
         // every wave's last fragments are in registers: the stages are free
         int cm0, cv0;
@@ -1128,13 +1252,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
                     store_one(j);
             }
         } else {
-#pragma unroll
-            for (int a = 0; a < AV; ++a)
-#pragma unroll
-                for (int bm = 0; bm < AM; ++bm)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        acc[a][bm][e] = 0.0f;
+            zero_acc();
         }
         load_hidx(i + 2);
         if constexpr (REDUCE) {
@@ -1542,7 +1660,7 @@ hipError_t launch_persist(const void *H, const int32_t *idx, int64_t rows, const
     return hipGetLastError();
 }
 
-template <int NSPREAD, int DEFER, int NIMM, bool STORE = true, bool REDUCE = false>
+template <int NSPREAD, int DEFER, int NIMM, bool STORE = true, bool REDUCE = false, bool M16 = false>
 hipError_t launch_defer(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V, int64_t d,
                         void *out, int64_t ldo, int group_m, hipStream_t stream, float *pmax = nullptr,
                         int32_t *parg = nullptr, float *psum = nullptr)
@@ -1553,8 +1671,8 @@ hipError_t launch_defer(const void *H, const int32_t *idx, int64_t rows, const v
     const int64_t ntiles = ((V + 255) / 256) * ((rows + 255) / 256);
     int64_t grid = std::max<int64_t>(8, (cus / 8) * 8);
     grid = std::min<int64_t>(grid, ((ntiles + 7) / 8) * 8);
-    hipLaunchKernelGGL((gather_gemm_bf16_defer_kernel<NSPREAD, DEFER, NIMM, STORE, REDUCE>), dim3((unsigned)grid),
-                       dim3(512), 0, stream, (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V,
+    hipLaunchKernelGGL((gather_gemm_bf16_defer_kernel<NSPREAD, DEFER, NIMM, STORE, REDUCE, M16>),
+                       dim3((unsigned)grid), dim3(512), 0, stream, (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V,
                        (int32_t)d, (__bf16 *)out, ldo, group_m, pmax, parg, psum);
     return hipGetLastError();
 }
@@ -1601,6 +1719,8 @@ bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V)
     case kVariantBf16DeferS8:
     case kVariantBf16DeferS4I8:
     case kVariantBf16DeferS16:
+    case kVariantBf16M16:
+    case kVariantBf16M16S1:
         return ((rows + 255) / 256) * ((V + 255) / 256) <= 0x7fffffffLL;
     case kVariantBf16LowM:
         return rows <= 64;
@@ -1612,14 +1732,20 @@ bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V)
 hipError_t launch_logits_argmax_lse(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V,
                                     int64_t d, void *out, int64_t ldo, float *pmax, int32_t *parg, float *psum,
                                     float *row_max, int32_t *row_argmax, float *row_lse, int group_m,
-                                    hipStream_t stream)
+                                    bool m16, hipStream_t stream)
 {
     if (group_m <= 0)
         group_m = kDefaultGroupM;
-    const hipError_t e =
-        out ? launch_defer<2, 4, 8, true, true>(H, idx, rows, W, V, d, out, ldo, group_m, stream, pmax, parg, psum)
-            : launch_defer<2, 4, 8, false, true>(H, idx, rows, W, V, d, nullptr, ldo, group_m, stream, pmax, parg,
-                                                 psum);
+    hipError_t e;
+    if (m16)
+        e = out ? launch_defer<1, 1, 16, true, true, true>(H, idx, rows, W, V, d, out, ldo, group_m, stream, pmax,
+                                                           parg, psum)
+                : launch_defer<1, 1, 16, false, true, true>(H, idx, rows, W, V, d, nullptr, ldo, group_m, stream,
+                                                            pmax, parg, psum);
+    else
+        e = out ? launch_defer<2, 4, 8, true, true>(H, idx, rows, W, V, d, out, ldo, group_m, stream, pmax, parg, psum)
+                : launch_defer<2, 4, 8, false, true>(H, idx, rows, W, V, d, nullptr, ldo, group_m, stream, pmax, parg,
+                                                     psum);
     if (e != hipSuccess)
         return e;
     const int ncol = (int)((V + 255) / 256);
@@ -1675,6 +1801,12 @@ hipError_t launch_gather_gemm(int variant, const void *H, const int32_t *idx, in
         return out_bf16 ? launch_defer<2, 4, 8>(H, idx, rows, W, V, d, out, ldo, group_m, stream) : hipErrorInvalidValue;
     case kVariantBf16DeferS16:
         return out_bf16 ? launch_defer<2, 16, 0>(H, idx, rows, W, V, d, out, ldo, group_m, stream) : hipErrorInvalidValue;
+    case kVariantBf16M16:
+        return out_bf16 ? launch_defer<2, 1, 16, true, false, true>(H, idx, rows, W, V, d, out, ldo, group_m, stream)
+                        : hipErrorInvalidValue;
+    case kVariantBf16M16S1:
+        return out_bf16 ? launch_defer<1, 1, 16, true, false, true>(H, idx, rows, W, V, d, out, ldo, group_m, stream)
+                        : hipErrorInvalidValue;
     case kVariantBf16PersistK64:
         return launch_persist<64, 2, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
     case kVariantBf16PersistK64S4:

@@ -36,7 +36,9 @@ enum LogitsVariant : int {
     kVariantBf16DeferS8 = 15,      // persistent 8-wave, bf16 out, tile stores spread over 8 K steps
     kVariantBf16DeferS4I8 = 16,    // ... half the stores at once, half over 4 K steps
     kVariantBf16DeferS16 = 17,     // ... stores spread over 16 K steps
-    kNumVariants = 18,
+    kVariantBf16M16 = 18,          // persistent 8-wave, 16 x 16 x 32 MFMA, bf16 out, stores at each tile's end
+    kVariantBf16M16S1 = 19,        // ... refill DMA in one k sub-step
+    kNumVariants = 20,
 };
 
 // Default number of row tiles that share the W slabs of one XCD (tile order).
@@ -58,7 +60,7 @@ hipError_t launch_gather_gemm(int variant, const void *H, const int32_t *idx, in
 hipError_t launch_logits_argmax_lse(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V,
                                     int64_t d, void *out, int64_t ldo, float *pmax, int32_t *parg, float *psum,
                                     float *row_max, int32_t *row_argmax, float *row_lse, int group_m,
-                                    hipStream_t stream);
+                                    bool m16, hipStream_t stream);
 
 // FP8 LM head.  Quantize `rows` rows of X ([*, d], bf16 or fp32, d % 8 == 0; row r is
 // source row row_idx[r], or r when row_idx is null) to E4M3 codes q ([rows, d]) and

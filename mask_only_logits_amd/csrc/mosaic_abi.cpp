@@ -43,7 +43,8 @@ int64_t checked_bytes(int64_t rows, int64_t V, int64_t esize)
 
 // Debug/tuning override read on every call:
 // MOSAIC_TUNE="variant=<n>,group_m=<g>,waves=<w>" (waves: the FP8 kernel's 4 or 8).
-// A forced variant that cannot run the call's shape is ignored.
+// A forced variant that cannot run the call's shape is ignored.  For the fused consumer,
+// variant=16 selects its 32 x 32 x 16 MFMA form (default: 16 x 16 x 32).
 struct Tune {
     int variant = -1;
     int group_m = 0;
@@ -117,7 +118,9 @@ bool variant_can_run(int v, int64_t M, int64_t d, mosaic_dtype_t in, mosaic_dtyp
     case mosaic::kVariantBf16W8K64: return bf16_in && d % 64 == 0 && small_d;
     case mosaic::kVariantBf16DeferS8:
     case mosaic::kVariantBf16DeferS4I8:
-    case mosaic::kVariantBf16DeferS16: return in == MOSAIC_BF16 && out == MOSAIC_BF16 && d % 64 == 0 && small_d;
+    case mosaic::kVariantBf16DeferS16:
+    case mosaic::kVariantBf16M16:
+    case mosaic::kVariantBf16M16S1: return in == MOSAIC_BF16 && out == MOSAIC_BF16 && d % 64 == 0 && small_d;
     case mosaic::kVariantBf16W8K32S4:
     case mosaic::kVariantBf16PersistK32: return bf16_in && d % 32 == 0 && small_d;
     case mosaic::kVariantBf16K32S3:
@@ -140,8 +143,8 @@ int pick_variant(int64_t M, int64_t V, int64_t d, mosaic_dtype_t in, mosaic_dtyp
     // order, so the choice (made per launch from its row count) never changes a bit.
     if (variant_can_run(mosaic::kVariantBf16LowM, M, d, in, out))
         return mosaic::kVariantBf16LowM;
-    if (variant_can_run(mosaic::kVariantBf16DeferS4I8, M, d, in, out))
-        return mosaic::kVariantBf16DeferS4I8;
+    if (variant_can_run(mosaic::kVariantBf16M16S1, M, d, in, out))
+        return mosaic::kVariantBf16M16S1;
     if (variant_can_run(mosaic::kVariantBf16W8K64S2, M, d, in, out))
         return mosaic::kVariantBf16W8K64S2;
     if (variant_can_run(mosaic::kVariantBf16PersistK32, M, d, in, out))
@@ -362,14 +365,15 @@ mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_
     const mosaic_status_t ck = check_idx_if_asked(idx, M, L, (hipStream_t)stream);
     if (ck != MOSAIC_OK)
         return ck;
-    const int group_m = read_tune().group_m;
+    const Tune t = read_tune();
+    const bool m16 = t.variant != mosaic::kVariantBf16DeferS4I8;   // 32 x 32 x 16 form on request
     for (int64_t k = 0; k < K; ++k) {
         const int64_t r0 = k * C;
         const int64_t r1 = (r0 + C < M) ? r0 + C : M;
         void *chunk_out = out ? (char *)out + r0 * V * 2 : nullptr;
         const hipError_t e = mosaic::launch_logits_argmax_lse(H, idx + r0, r1 - r0, W, V, d, chunk_out, V, pmax,
                                                               parg, psum, row_max + r0, row_argmax + r0,
-                                                              row_lse + r0, group_m, (hipStream_t)stream);
+                                                              row_lse + r0, t.group_m, m16, (hipStream_t)stream);
         if (e != hipSuccess)
             return MOSAIC_ERR_DEVICE;
     }

@@ -184,3 +184,25 @@ def test_other_workloads_sampled_rows(m, name):
     rows = sample_rows(idx.size, wl.chunk_rows, 4, seed=3)
     rows = rows[np.linspace(0, rows.size - 1, min(rows.size, 10)).astype(int)]
     _check(got, wl.H, idx, wl.W, rows=rows, what=name)
+
+
+@pytest.mark.parametrize("L,d,V,M,C", [CASES[0], CASES[2], CASES[4], CASES[6]])
+def test_mfma_forms_match(m, monkeypatch, L, d, V, M, C):
+    # the 32 x 32 x 16 MFMA form of the fused kernel (variant=16) against the default
+    # 16 x 16 x 32 form: same fp32 logits, so the row max, argmax and stored logits are
+    # identical; the exp sums are added in another order (oracle bound only)
+    wl = inputs.make_random(L * 7 + d + V + M, L=L, d=d, V=V, M=M, dtype="bf16")
+    idx, idx_d = _idx(wl)
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    got = m.mosaic_masked_logits_argmax_lse(H, idx_d, W, chunk_rows=C, store_logits=True)
+    only = m.mosaic_masked_logits_argmax_lse(H, idx_d, W, chunk_rows=C)
+    monkeypatch.setenv("MOSAIC_TUNE", "variant=16")
+    ref = m.mosaic_masked_logits_argmax_lse(H, idx_d, W, chunk_rows=C, store_logits=True)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("MOSAIC_TUNE")
+    assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
+    assert torch.equal(got[3], ref[3])
+    for x, y in zip(only[:3], got[:3]):
+        assert torch.equal(x, y)
+    _check(got, wl.H, idx, wl.W, what=f"{L},{d},{V},{M},{C}")
+    _check(ref, wl.H, idx, wl.W, what=f"32x32 form {L},{d},{V},{M},{C}")
