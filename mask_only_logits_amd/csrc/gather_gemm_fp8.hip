@@ -220,7 +220,7 @@ gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__
         const i32x4_t up = *(const i32x4_t *)(smem + (addr ^ (64 * s + 16)));
         return i32x8_t{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
     };
-    auto load_frags = [&](int so, int s, i32x8_t (&af)[AV], i32x8_t (&bf)[AM]) {
+    auto load_frags = [&](int so, int s, i32x8_t (&af)[AV], i32x8_t (&bf)[AM]) __attribute__((always_inline)) {
 #pragma unroll
         for (int a = 0; a < AV; ++a)
             af[a] = frag(a_addr + so + a * 32 * ROW_BYTES, s);
@@ -228,13 +228,37 @@ gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__
         for (int bm = 0; bm < AM; ++bm)
             bf[bm] = frag(b_addr + so + bm * 32 * ROW_BYTES, s);
     };
-    auto mma = [&](const i32x8_t (&af)[AV], const i32x8_t (&bf)[AM]) {
+    auto mma = [&](const i32x8_t (&af)[AV], const i32x8_t (&bf)[AM]) __attribute__((always_inline)) {
 #pragma unroll
         for (int a = 0; a < AV; ++a)
 #pragma unroll
             for (int bm = 0; bm < AM; ++bm)
                 acc[a][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[a], bf[bm], acc[a][bm], 0, 0, 0,
                                                                              127, 0, 127);
+    };
+    // MFMAs on fragment buffer `cur` while the fragments of k sub-step s of stage so are
+    // read.  Four waves: both operands double-buffered.  Eight waves (256 registers per
+    // wave): the A fragments are single-buffered, block a's next fragment being read right
+    // after the last MFMA of its row, which keeps the wave within its registers.
+    constexpr bool ROLL = NW == 8;
+    auto mma_load = [&](int so, int s, int cur, i32x8_t (&af)[2][AV], i32x8_t (&bf)[2][AM])
+                        __attribute__((always_inline)) {
+        if constexpr (ROLL) {
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm)
+                bf[cur ^ 1][bm] = frag(b_addr + so + bm * 32 * ROW_BYTES, s);
+#pragma unroll
+            for (int a = 0; a < AV; ++a) {
+#pragma unroll
+                for (int bm = 0; bm < AM; ++bm)
+                    acc[a][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[0][a], bf[cur][bm], acc[a][bm], 0,
+                                                                                 0, 0, 127, 0, 127);
+                af[0][a] = frag(a_addr + so + a * 32 * ROW_BYTES, s);
+            }
+        } else {
+            load_frags(so, s, af[cur ^ 1], bf[cur ^ 1]);
+            mma(af[cur], bf[cur]);
+        }
     };
     constexpr int NFR = 2 * (AV + AM);
     auto interleave = [&](int nvm) {
@@ -245,10 +269,28 @@ gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
         }
+        if constexpr (ROLL) {
+            // the B reads early, then each A read after its row's MFMAs
 #pragma unroll
-        for (int i = 0; i < NFR; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int bm = 0; bm < AM; ++bm) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            const int used = nvm + AM;
+#pragma unroll
+            for (int a = 0; a < AV; ++a) {
+#pragma unroll
+                for (int c = 0; c < AM; ++c)
+                    if (a * AM + c >= used)
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NFR; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
         }
     };
 
@@ -273,8 +315,7 @@ gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__
         // sub-step 0: the rest of the previous refill, the fragments of sub-step 1
         if (pending)
             issue_part(pso, pkt, 1);
-        load_frags(rd, 1, af[1], bf[1]);
-        mma(af[0], bf[0]);
+        mma_load(rd, 1, 0, af, bf);
         interleave(pending ? PER : 0);
         __builtin_amdgcn_sched_barrier(0);
         wait_vm<0>();
@@ -285,8 +326,7 @@ gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__
         pkt = kt + NSTAGE;
         pending = true;
         const int nx = (rd + STAGE == NSTAGE * STAGE) ? 0 : rd + STAGE;
-        load_frags(nx, 0, af[0], bf[0]);
-        mma(af[1], bf[1]);
+        mma_load(nx, 0, 1, af, bf);
         interleave(PER);
         __builtin_amdgcn_sched_barrier(0);
         rd = nx;
@@ -295,28 +335,35 @@ gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__
         if (pending)
             issue_part(pso, pkt, 1);
         pending = false;
-        load_frags(rd, 1, af[1], bf[1]);
-        mma(af[0], bf[0]);
-        if (kt + 1 < nk) {
-            wait_vm<0>();
-            bar();
-            rd = (rd + STAGE == NSTAGE * STAGE) ? 0 : rd + STAGE;
-            load_frags(rd, 0, af[0], bf[0]);
+        mma_load(rd, 1, 0, af, bf);
+        if constexpr (ROLL) {
+            // one MFMA sequence for both cases; after the last K tile its reads are unused
+            if (kt + 1 < nk) {
+                wait_vm<0>();
+                bar();
+                rd = (rd + STAGE == NSTAGE * STAGE) ? 0 : rd + STAGE;
+            }
+            mma_load(rd, 0, 1, af, bf);
+        } else {
+            if (kt + 1 < nk) {
+                wait_vm<0>();
+                bar();
+                rd = (rd + STAGE == NSTAGE * STAGE) ? 0 : rd + STAGE;
+                load_frags(rd, 0, af[0], bf[0]);
+            }
+            mma(af[1], bf[1]);
         }
-        mma(af[1], bf[1]);
     }
 
     // epilogue: lane holds vocabulary entries v0 + wv*WV + 32a + 8gq + 4hi + (0..3) of
-    // masked row m0 + wm*WM + 32bm + fr.  Four waves (256 accumulators, registers to
-    // spare): after scaling and rounding, permlane32_swap gives lanes 0-31 entries 0-7 /
-    // 16-23 of a 32-entry block and lanes 32-63 entries 8-15 / 24-31, and every lane
-    // stores 16 bytes.  Eight waves: the swap's extra registers spill, so each lane
-    // stores its 4 entries (8 bytes) directly (measured faster for each wave count).
+    // masked row m0 + wm*WM + 32bm + fr.  After scaling and rounding, permlane32_swap gives
+    // lanes 0-31 entries 0-7 / 16-23 of a 32-entry block and lanes 32-63 entries 8-15 /
+    // 24-31, and every lane stores 16 bytes.
     auto pack2 = [](float x, float y) {
         const __bf16 a = static_cast<__bf16>(x), b = static_cast<__bf16>(y);
         return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
     };
-    if constexpr (NW == 4) {
+    {
         const bool vec_ok = ((uintptr_t)out & 15) == 0 && (ldo & 7) == 0;
 #pragma unroll
         for (int bm = 0; bm < AM; ++bm) {
@@ -360,34 +407,6 @@ gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__
                         for (int e = 0; e < 8; ++e)
                             if (v + e < V)
                                 o[e] = __builtin_bit_cast(__bf16, (uint16_t)(w4[e >> 1] >> (16 * (e & 1))));
-                    }
-                }
-            }
-        }
-    } else {
-        const bool vec_ok = ((uintptr_t)out & 7) == 0 && (ldo & 3) == 0;
-#pragma unroll
-        for (int bm = 0; bm < AM; ++bm) {
-            const int row = m0 + wm * WM + bm * 32 + fr;
-            if (row >= rows)
-                continue;
-            const float h = hs[row];
-#pragma unroll
-            for (int a = 0; a < AV; ++a) {
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const int v = v0 + wv * WV + a * 32 + gq * 8 + hi * 4;
-                    __bf16 *o = out + (int64_t)row * ldo + v;
-                    if (vec_ok && v + 3 < V) {
-                        const f32x4_t w = *(const f32x4_t *)(ws + v);
-                        *(uint2 *)o = make_uint2(
-                            pack2(acc[a][bm][gq * 4 + 0] * (h * w[0]), acc[a][bm][gq * 4 + 1] * (h * w[1])),
-                            pack2(acc[a][bm][gq * 4 + 2] * (h * w[2]), acc[a][bm][gq * 4 + 3] * (h * w[3])));
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (v + e < V)
-                                o[e] = static_cast<__bf16>(acc[a][bm][gq * 4 + e] * (h * ws[v + e]));
                     }
                 }
             }
