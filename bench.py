@@ -80,6 +80,19 @@ def measured_traffic(workload: str, path: str = "logits"):
     return t.get("bytes_per_launch")
 
 
+def host_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count()}
+
+
 def cpu_baseline(wl, idx_np, target_s: float, path: str = "logits"):
     """Time the oracle on a bounded sample of masked rows (the first rows of idx)."""
     import oracle
@@ -190,6 +203,10 @@ def main():
     ap.add_argument("--profile-copy-mib", type=int, default=0,
                     help="after the timed steps, run a plain elementwise copy of this many MiB three times "
                          "(a kernel of known traffic that calibrates rocprofv3's FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--flush-mib", type=int, default=-1,
+                    help="after the timed steps, time as many again with a cache-evicting pass over a buffer of "
+                         "this many MiB before each (reported under detail.flushed); default: 512 for the "
+                         "HBM-bound low-M kernel, else off")
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="summarize rocprofv3 CSV output found under DIR into profiles/ and exit")
     ap.add_argument("--path", choices=("logits", "argmax_lse", "dense_select", "fp8"), default="logits",
@@ -327,6 +344,7 @@ def main():
     gemm_ms = [a[1].elapsed_time(a[2]) for a in ev]
     compact_ms = [a[0].elapsed_time(a[1]) for a in ev]
     gemm_avg = float(np.mean(gemm_ms))
+    gemm_median = float(np.median(gemm_ms))
     value = flop / (ms_per_step / 1e3) / 1e12
     # the kernel's own FLOP: the dense baseline multiplies all L rows
     achieved = (2.0 * L * d * V if dense else flop) / (gemm_avg / 1e3) / 1e12
@@ -380,13 +398,38 @@ def main():
                    "out_dtype": "per-row f32 max / i32 argmax / f32 lse" if consumer else wl.out_dtype,
                    "accumulate": "fp32", "path": args.path},
         "roofline": roofline,
-        "detail": {"gemm_ms_per_step": round(gemm_avg, 4), "gemm_ms_min": round(min(gemm_ms), 4),
+        "detail": {"gemm_ms_per_step": round(gemm_avg, 4), "gemm_ms_median": round(gemm_median, 4),
+                   "gemm_ms_min": round(min(gemm_ms), 4),
                    "compaction_readback_us": round(float(np.mean(compact_ms)) * 1e3, 2),
                    # logits buffers alive at once: [L, V] + the selected [M, V] (dense_select),
                    # the [M, V] output (logits), none (argmax_lse)
                    "peak_logits_bytes": int((L * V + M * V) * out.element_size()) if dense else
                    (0 if consumer else int(M * V * out.element_size()))},
     }
+    flush_mib = args.flush_mib if args.flush_mib >= 0 else (512 if variant == 6 else 0)
+    if flush_mib:
+        # W no longer partly in the caches from the previous step: read a buffer larger than
+        # the Infinity Cache before each step, outside the GEMM events (a read, so the flush
+        # leaves no dirty lines to be written back during the GEMM)
+        fl = torch.ones(flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        fsum = torch.empty((), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        fms = []
+        for i in range(args.steps):
+            torch.sum(fl, dim=0, dtype=torch.float32, out=fsum)
+            step(i)
+            torch.cuda.synchronize()
+            fms.append(ev[i][1].elapsed_time(ev[i][2]))
+        del fl
+        fmed = float(np.median(fms))
+        result["detail"]["flushed"] = {"flush_mib": flush_mib, "gemm_ms_median": round(fmed, 4),
+                                       "gemm_ms_min": round(min(fms), 4)}
+        if variant == 6:
+            result["detail"]["flushed"]["achieved_gbs"] = round(alg_bytes / (fmed / 1e3) / 1e9, 1)
+        else:
+            result["detail"]["flushed"]["achieved_tflops"] = round(flop / (fmed / 1e3) / 1e12, 2)
+        log(f"[bench] with a {flush_mib} MiB cache flush before each step: GEMM median {fmed:.3f} ms")
+
     if args.profile_copy_mib:
         n = args.profile_copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -404,6 +447,7 @@ def main():
         idx_np = idx[:M].cpu().numpy()
         log("[bench] timing the CPU oracle on a row sample ...")
         result["cpu_baseline"] = cpu_baseline(wl, idx_np, args.cpu_seconds, args.path)
+        result["detail"]["host"] = host_info()
         log(f"[bench] cpu_baseline {result['cpu_baseline']}")
     else:
         result["cpu_baseline"] = None
