@@ -11,9 +11,10 @@
 //  * Tile: 256 vocabulary rows x 256 masked rows per workgroup, K staged 64 deep
 //    (128 bytes per row).  Four waves, each owning a 128 x 128 sub-tile as 4 x 4 blocks
 //    of v_mfma_f32_32x32x16_bf16 (fp32 accumulators: 256 per lane), or eight waves (two
-//    per SIMD) of 128 x 64.  W is the MFMA A operand (vocabulary rows) and the gathered
-//    H rows are the B operand, so each lane's accumulators hold four consecutive
-//    vocabulary entries of one masked row.
+//    per SIMD) of 128 x 64, as 4 x 2 such blocks or, in the default bf16-output kernel,
+//    8 x 4 blocks of v_mfma_f32_16x16x32_bf16.  W is the MFMA A operand (vocabulary
+//    rows) and the gathered H rows are the B operand, so each lane's accumulators hold
+//    four consecutive vocabulary entries of one masked row.
 //  * Operands reach LDS with global_load_lds_dwordx4 (16 bytes per lane, written to
 //    LDS without passing through VGPRs).  The gather is free: each lane's source
 //    address is just H + idx[row] * d + k, and a 64-lane instruction fills 8 rows x
@@ -28,8 +29,9 @@
 //    tiles, ordered so that groups of GROUP_M row-tiles share one W slab in that XCD's
 //    L2.
 //  * Bit-identity across chunks: every output element is one accumulation chain over
-//    k = 0, 16, 32, ... in the same MFMA positions whatever the chunk, tile or row
-//    position, so splitting the rows into chunks never changes a bit.
+//    k in ascending order in the same MFMA positions whatever the chunk, tile or row
+//    position, so splitting the rows into chunks never changes a bit.  (The two MFMA
+//    shapes were measured to agree bit for bit as well.)
 //  * Variants of this design (one tile per workgroup; persistent per-XCD tile lists;
 //    deferred epilogue stores) and a low-M streaming kernel share the MFMA, operand
 //    roles and k order, so they all produce identical bits.

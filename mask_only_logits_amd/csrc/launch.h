@@ -37,7 +37,7 @@ enum LogitsVariant : int {
     kVariantBf16DeferS4I8 = 16,    // ... half the stores at once, half over 4 K steps
     kVariantBf16DeferS16 = 17,     // ... stores spread over 16 K steps
     kVariantBf16M16 = 18,          // persistent 8-wave, 16 x 16 x 32 MFMA, bf16 out, stores at each tile's end
-    kVariantBf16M16S1 = 19,        // ... refill DMA in one k sub-step
+    kVariantBf16M16S1 = 19,        // ... refill DMA in one k sub-step (the bf16-output default)
     kNumVariants = 20,
 };
 
@@ -56,7 +56,9 @@ hipError_t launch_gather_gemm(int variant, const void *H, const int32_t *idx, in
 // One chunk of the per-row consumer (bf16 in, d % 64 == 0): the persistent kernel
 // reduces every (row, 256-entry vocabulary tile) to a partial in pmax / parg / psum
 // ([ceil(V/256)][rows] each) and, when `out` is not null, also stores the bf16 logits;
-// a finish kernel combines the partials into row_max / row_argmax / row_lse.
+// a finish kernel combines the partials into row_max / row_argmax / row_lse.  m16 selects
+// the 16 x 16 x 32 MFMA form of the kernel (else 32 x 32 x 16); the two give the same
+// logits, maxima and argmax, and exp sums added in different orders.
 hipError_t launch_logits_argmax_lse(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V,
                                     int64_t d, void *out, int64_t ldo, float *pmax, int32_t *parg, float *psum,
                                     float *row_max, int32_t *row_argmax, float *row_lse, int group_m,
