@@ -47,17 +47,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the gather-GEMM sources with comments and blank lines removed, so that
-    a measured traffic figure stays attached to the code it was measured on."""
+def code_lines(text: str):
+    """The lines of a C/C++ source that carry code: comments and blank lines removed."""
     import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = []
+    for line in text.splitlines():
+        line = line.split("//", 1)[0].rstrip()
+        if line.strip():
+            out.append(line)
+    return out
+
+
+def kernel_source_hash() -> str:
+    """Hash of the gather-GEMM sources' code lines, so that a measured traffic figure
+    stays attached to the code it was measured on (comment edits keep it)."""
     h = hashlib.sha256()
     for f in ("gather_gemm.hip", "gather_gemm_fp8.hip", "mosaic_abi.cpp", "launch.h"):
         with open(os.path.join(ROOT, "mask_only_logits_amd", "csrc", f), encoding="utf-8") as fh:
-            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
-        for line in text.splitlines():
-            line = line.split("//", 1)[0].rstrip()
-            if line.strip():
+            for line in code_lines(fh.read()):
                 h.update(line.encode() + b"\n")
     return h.hexdigest()[:16]
 
@@ -66,12 +74,13 @@ def _profile_tag(workload: str, path: str) -> str:
     return workload if path == "logits" else f"{workload}_{path}"
 
 
-def measured_traffic(workload: str, path: str = "logits"):
+def measured_traffic(workload: str, path: str = "logits", prof_dir: str | None = None):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_gather_gemm_{_profile_tag(workload, path)}.json")
+    fname = os.path.join(prof_dir or os.path.join(ROOT, "profiles"),
+                         f"traffic_gather_gemm_{_profile_tag(workload, path)}.json")
     try:
-        with open(path, encoding="utf-8") as fh:
+        with open(fname, encoding="utf-8") as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
@@ -126,11 +135,13 @@ def _find(root, suffix):
     return sorted(out)
 
 
-def summarize_profile(root: str, workload: str, copy_mib: int, path: str = "logits"):
+def summarize_profile(root: str, workload: str, copy_mib: int, path: str = "logits", prof_dir: str | None = None):
     """Write profiles/ summaries from rocprofv3 output under `root`: kernel_stats
     (--kernel-trace --stats) and counter_collection (--pmc) CSV files.  `root/commands.txt`,
-    if present, holds the rocprofv3 command lines that produced them; it is copied in."""
-    prof = os.path.join(ROOT, "profiles")
+    if present, holds the rocprofv3 command lines that produced them; it is copied in.
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read for the
+    copy probe of `copy_mib` MiB, a kernel that reads and writes exactly that much."""
+    prof = prof_dir or os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
     stats = _find(root, "kernel_stats.csv")
     counters = _find(root, "counter_collection.csv")
