@@ -72,7 +72,8 @@ const char *mosaic_status_string(mosaic_status_t s);
  *                     ascending order (entries from M on are left untouched).
  *   count   int32[1]  on return M.
  * L == 0 writes count = 0.  L >= 2^31 -> UNSUPPORTED.  Null tokens/idx with L > 0,
- * null count, or L < 0 -> INVALID_ARG.  Runs as a single workgroup (one launch). */
+ * null count, or L < 0 -> INVALID_ARG.  One launch of at most 64 workgroups; needs no
+ * workspace. */
 mosaic_status_t mosaic_mask_compact(const int32_t *tokens, int64_t L, int32_t mask_id,
                                     int32_t *idx, int32_t *count, void *stream);
 

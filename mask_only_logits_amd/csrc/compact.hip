@@ -6,17 +6,20 @@
 // "扩散大语言模型内存优化：Mosaic系统突破与实践", §2.2).  This kernel builds that
 // list from token ids (or flags) on the device.
 //
-// Design (gfx950, wave64): one workgroup of 16 waves walks the sequence in tiles of
-// 16 x 64 x ITEMS positions.  Wave w owns a contiguous run of 64*ITEMS positions of
-// the tile; for each group of 64 it takes a 64-bit ballot of "masked", so the rank
-// of a lane among the masked lanes before it is mbcnt(ballot) and the wave's count is
-// popcount(ballot).  The 16 wave counts are scanned through LDS, which gives every
-// wave its output offset inside the tile; a running base carries the count across
-// tiles.  Positions are therefore written in ascending order, and the result is
-// unique (bit-identical to any correct compaction).  The whole input is read once
-// with coalesced loads; at the sizes of a sequence (<= 2^17 positions, 512 KiB)
-// a single workgroup finishes in a few microseconds, so no cross-workgroup scan
-// (and no workspace) is needed.
+// Design (gfx950, wave64): the sequence is cut into G <= 64 segments, a multiple of
+// the tile size each, one workgroup of 16 waves per segment.  A workgroup first counts
+// the masked positions before its segment: it re-reads that prefix itself with 16-byte
+// loads (the prefix is at most the whole input, 512 KiB for 2^17 positions, and comes
+// from L2 and the Infinity Cache), so no cross-workgroup scan, flag protocol or
+// workspace is needed, and the result does not depend on timing.  It then walks its
+// segment in tiles of 16 x 64 x ITEMS positions.  Wave w owns a contiguous run of
+// 64*ITEMS positions of the tile; for each group of 64 it takes a 64-bit ballot of
+// "masked", so the rank of a lane among the masked lanes before it is mbcnt(ballot)
+// and the wave's count is popcount(ballot).  The 16 wave counts are scanned through
+// LDS, which gives every wave its output offset inside the tile; a running base
+// carries the count across tiles.  Positions are therefore written in ascending order,
+// and the result is unique (bit-identical to any correct compaction).  The last
+// workgroup writes the total.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -37,18 +40,80 @@ __device__ __forceinline__ uint32_t rank_below(uint64_t mask)
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+constexpr int64_t kTile = (int64_t)kThreads * kItems;   // positions per tile
+constexpr int kMaxSegments = 64;
+
+// Masked positions among [0, n) counted by this thread's share (n % 16 == 0).
+template <typename T, bool kFlags>
+__device__ __forceinline__ uint32_t count_prefix(const T *__restrict__ in, int64_t n, int32_t mask_id)
+{
+    uint32_t c = 0;
+    const bool vec = ((uintptr_t)in & 15) == 0;
+    if constexpr (kFlags) {
+        if (vec) {
+            const uint4 *v = (const uint4 *)in;
+            const int64_t n16 = n / 16;
+            auto nz = [](uint32_t w) {
+                return (uint32_t)((w & 0xffu) != 0) + (uint32_t)((w & 0xff00u) != 0) +
+                       (uint32_t)((w & 0xff0000u) != 0) + (uint32_t)((w & 0xff000000u) != 0);
+            };
+#pragma unroll 4
+            for (int64_t i = threadIdx.x; i < n16; i += kThreads) {
+                const uint4 x = v[i];
+                c += nz(x.x) + nz(x.y) + nz(x.z) + nz(x.w);
+            }
+            return c;
+        }
+#pragma unroll 4
+        for (int64_t p = threadIdx.x; p < n; p += kThreads)
+            c += in[p] != 0;
+    } else {
+        if (vec) {
+            const int4 *v = (const int4 *)in;
+            const int64_t n4 = n / 4;
+#pragma unroll 4
+            for (int64_t i = threadIdx.x; i < n4; i += kThreads) {
+                const int4 x = v[i];
+                c += (uint32_t)(x.x == mask_id) + (uint32_t)(x.y == mask_id) + (uint32_t)(x.z == mask_id) +
+                     (uint32_t)(x.w == mask_id);
+            }
+            return c;
+        }
+#pragma unroll 4
+        for (int64_t p = threadIdx.x; p < n; p += kThreads)
+            c += in[p] == mask_id;
+    }
+    return c;
+}
+
 template <typename T, bool kFlags>
 __global__ __launch_bounds__(kThreads) void mask_compact_kernel(const T *__restrict__ in, int64_t L,
-                                                                int32_t mask_id,
+                                                                int32_t mask_id, int64_t seg,
                                                                 int32_t *__restrict__ idx,
                                                                 int32_t *__restrict__ count)
 {
     __shared__ uint32_t wave_count[kWaves];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    uint32_t base = 0;   // masked positions before the current tile (same in every thread)
+    const int64_t s0 = (int64_t)blockIdx.x * seg;
+    const int64_t s1 = s0 + seg < L ? s0 + seg : L;
 
-    for (int64_t t0 = 0; t0 < L; t0 += (int64_t)kThreads * kItems) {
+    // masked positions before this segment: per-thread counts, summed over the wave and
+    // then over the 16 waves
+    uint32_t c = count_prefix<T, kFlags>(in, s0, mask_id);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        c += __shfl_xor(c, o, 64);
+    if (lane == 0)
+        wave_count[wave] = c;
+    __syncthreads();
+    uint32_t base = 0;   // masked positions before the current tile (same in every thread)
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+        base += wave_count[w];
+    __syncthreads();     // wave_count is rewritten by the first tile
+
+    for (int64_t t0 = s0; t0 < s1; t0 += kTile) {
         const int64_t w0 = t0 + (int64_t)wave * 64 * kItems;
         uint64_t masks[kItems];
         uint32_t wave_total = 0;
@@ -56,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void mask_compact_kernel(const T *__restr
         for (int j = 0; j < kItems; ++j) {
             const int64_t p = w0 + j * 64 + lane;
             bool hit = false;
-            if (p < L) {
+            if (p < s1) {
                 if constexpr (kFlags)
                     hit = in[p] != 0;
                 else
@@ -86,8 +151,18 @@ __global__ __launch_bounds__(kThreads) void mask_compact_kernel(const T *__restr
         }
         base += tile_total;
     }
-    if (threadIdx.x == 0)
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0)
         *count = (int32_t)base;
+}
+
+// G segments of seg positions (a multiple of the tile), G <= kMaxSegments, G * seg >= L;
+// at least one workgroup, so that an empty input still writes its count.
+void segments(int64_t L, int64_t &seg, unsigned &G)
+{
+    const int64_t tiles = std::max<int64_t>(1, (L + kTile - 1) / kTile);
+    const int64_t g = std::min<int64_t>(tiles, kMaxSegments);
+    seg = (tiles + g - 1) / g * kTile;
+    G = (unsigned)std::max<int64_t>(1, (L + seg - 1) / seg);
 }
 
 // idx_offsets[s] = number of masked positions before seq_offsets[s], found by binary
@@ -146,16 +221,22 @@ hipError_t launch_idx_range_check(const int32_t *idx, int64_t M, int64_t L, int3
 hipError_t launch_mask_compact(const int32_t *tokens, int64_t L, int32_t mask_id, int32_t *idx,
                                int32_t *count, hipStream_t stream)
 {
-    hipLaunchKernelGGL((mask_compact_kernel<int32_t, false>), dim3(1), dim3(kThreads), 0, stream,
-                       tokens, L, mask_id, idx, count);
+    int64_t seg;
+    unsigned G;
+    segments(L, seg, G);
+    hipLaunchKernelGGL((mask_compact_kernel<int32_t, false>), dim3(G), dim3(kThreads), 0, stream,
+                       tokens, L, mask_id, seg, idx, count);
     return hipGetLastError();
 }
 
 hipError_t launch_mask_compact_flags(const uint8_t *flags, int64_t L, int32_t *idx, int32_t *count,
                                      hipStream_t stream)
 {
-    hipLaunchKernelGGL((mask_compact_kernel<uint8_t, true>), dim3(1), dim3(kThreads), 0, stream,
-                       flags, L, 0, idx, count);
+    int64_t seg;
+    unsigned G;
+    segments(L, seg, G);
+    hipLaunchKernelGGL((mask_compact_kernel<uint8_t, true>), dim3(G), dim3(kThreads), 0, stream,
+                       flags, L, 0, seg, idx, count);
     return hipGetLastError();
 }
 
@@ -165,8 +246,11 @@ hipError_t launch_mask_compact_batched(const int32_t *tokens, int64_t L, const i
 {
     // Ascending global positions are already grouped by sequence, so the batched list
     // is the flat compaction; its total goes to idx_offsets[nseq].
-    hipLaunchKernelGGL((mask_compact_kernel<int32_t, false>), dim3(1), dim3(kThreads), 0, stream,
-                       tokens, L, mask_id, idx, idx_offsets + nseq);
+    int64_t seg;
+    unsigned G;
+    segments(L, seg, G);
+    hipLaunchKernelGGL((mask_compact_kernel<int32_t, false>), dim3(G), dim3(kThreads), 0, stream,
+                       tokens, L, mask_id, seg, idx, idx_offsets + nseq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
