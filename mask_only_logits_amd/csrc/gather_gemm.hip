@@ -765,6 +765,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     constexpr int NFR = AV + AM;
     constexpr int NST = M16 ? AV * AM / 2 : AV * AM * 2;   // 16-byte stores per lane and tile
     constexpr int HOOK_S = NSUB > 2 ? 1 : 0;  // k sub-step that issues a step's deferred stores
+    constexpr int EARLY = 1;                  // 16 x 16: rows whose next A fragment is read early
     using acc_t = typename std::conditional<M16, f32x4_t, f32x16_t>::type;
     static_assert(NSPREAD >= 1 && NSPREAD <= NSUB && NDMA % NSPREAD == 0, "spread");
     static_assert(NIMM >= 0 && NIMM <= NST && DEFER >= 1 && (NST - NIMM) % DEFER == 0, "defer");
@@ -923,10 +924,18 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
                 bf[cur ^ 1][bm] = *(const bf16x8_t *)(smem + bb + bm * MB * ROW_BYTES);
 #pragma unroll
             for (int a = 0; a < AV; ++a) {
+                // the last row reads its next fragment before its MFMAs (into a spare
+                // register): the reads of a stage must be complete at the step's barrier, and
+                // this way the wave's last read is followed by MFMAs instead of the wait
+                // (measured +1.5%; reading the last two or four rows early gains no more)
+                const bool early = a >= AV - EARLY;
+                bf16x8_t nxt;
+                if (early)
+                    nxt = *(const bf16x8_t *)(smem + ab + a * MB * ROW_BYTES);
 #pragma unroll
                 for (int bm = 0; bm < AM; ++bm)
                     acc[a][bm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][a], bf[cur][bm], acc[a][bm], 0, 0, 0);
-                af[0][a] = *(const bf16x8_t *)(smem + ab + a * MB * ROW_BYTES);
+                af[0][a] = early ? nxt : *(const bf16x8_t *)(smem + ab + a * MB * ROW_BYTES);
             }
         } else {
             load_frags(rw, rh, s, af[cur ^ 1], bf[cur ^ 1]);
@@ -935,7 +944,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     };
     // Instruction order of one k sub-step: each refill DMA issue beside an MFMA, then the
     // fragment reads spread over the MFMAs (16 x 16: the B reads first, then each A read
-    // after its row's MFMAs).
+    // after its row's MFMAs, the last row's before them).
     auto interleave = [&](int nvm) {
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) {
@@ -953,11 +962,14 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
             const int used = nvm + AM;
 #pragma unroll
             for (int a = 0; a < AV; ++a) {
+                if (a >= AV - EARLY)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
                 for (int c = 0; c < AM; ++c)
                     if (a * AM + c >= used)
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (a < AV - EARLY)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
         } else {
 #pragma unroll
