@@ -85,7 +85,10 @@ def test_parity_lowm(m, dt_out, L, d, V, M):
 
 @pytest.mark.parametrize("M,d,V,out", [(20, 3584, 5000, "bf16"), (64, 256, 1001, "f32"), (700, 512, 1000, "bf16"),
                                        (1, 64, 300, "bf16"), (1000, 192, 40001, "bf16"), (777, 128, 30000, "f32"),
-                                       (600, 64, 70000, "bf16"), (600, 1280, 70000, "bf16")])
+                                       (600, 64, 70000, "bf16"), (600, 1280, 70000, "bf16"),
+                                       # whole tiles (rows and V multiples of 256), several per workgroup
+                                       (1024, 512, 65536, "bf16"), (1024, 64, 65536, "bf16"),
+                                       (2048, 128, 32768, "bf16")])
 def test_bf16_variants_bit_identical(m, monkeypatch, M, d, V, out):
     # every bf16 MFMA variant accumulates each output in the same MFMA k order
     wl = inputs.make_random(M + d + V, L=max(M, 300), d=d, V=V, M=M, dtype="bf16")
