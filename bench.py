@@ -41,6 +41,7 @@ METRIC = "mask-only logits TFLOP/s (2·M·d·V) and % bf16 MFMA peak at L=32k, d
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+LOWM_VARIANTS = (6, 20)        # the W-streaming low-M kernels: HBM-bound
 
 
 def log(*a):
@@ -375,12 +376,12 @@ def main():
         # the dense baseline's own work: all L rows
         alg_bytes = launches * V * d * esize_in + L * d * esize_in + (L + 2 * M) * V * out.element_size()
     traffic = measured_traffic(args.workload, args.path)
-    kernel = "gather_gemm_fp8_kernel" if fp8 else "gather_gemm_bf16_defer_kernel" if consumer else {0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel", 6: "gather_gemm_lowm_kernel",
+    kernel = "gather_gemm_fp8_kernel" if fp8 else "gather_gemm_bf16_defer_kernel" if consumer else {0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel", 6: "gather_gemm_lowm_kernel", 20: "gather_gemm_lowm_shared_kernel",
               9: "gather_gemm_bf16_persist_kernel", 10: "gather_gemm_bf16_persist_kernel",
               11: "gather_gemm_bf16_persist_kernel", 15: "gather_gemm_bf16_defer_kernel",
               16: "gather_gemm_bf16_defer_kernel", 17: "gather_gemm_bf16_defer_kernel",
               18: "gather_gemm_bf16_defer_kernel", 19: "gather_gemm_bf16_defer_kernel"}.get(variant, "gather_gemm_bf16_kernel")
-    if variant == 6:
+    if variant in LOWM_VARIANTS:
         # streaming W is the bound: algorithmic bytes per launch over the launch time
         achieved_gbs = alg_bytes / launches / (gemm_avg / launches / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -417,7 +418,7 @@ def main():
                    "peak_logits_bytes": int((L * V + M * V) * out.element_size()) if dense else
                    (0 if consumer else int(M * V * out.element_size()))},
     }
-    flush_mib = args.flush_mib if args.flush_mib >= 0 else (512 if variant == 6 else 0)
+    flush_mib = args.flush_mib if args.flush_mib >= 0 else (512 if variant in LOWM_VARIANTS else 0)
     if flush_mib:
         # W no longer partly in the caches from the previous step: read a buffer larger than
         # the Infinity Cache before each step, outside the GEMM events (a read, so the flush
@@ -435,7 +436,7 @@ def main():
         fmed = float(np.median(fms))
         result["detail"]["flushed"] = {"flush_mib": flush_mib, "gemm_ms_median": round(fmed, 4),
                                        "gemm_ms_min": round(min(fms), 4)}
-        if variant == 6:
+        if variant in LOWM_VARIANTS:
             result["detail"]["flushed"]["achieved_gbs"] = round(alg_bytes / (fmed / 1e3) / 1e9, 1)
         else:
             result["detail"]["flushed"]["achieved_tflops"] = round(flop / (fmed / 1e3) / 1e12, 2)

@@ -1367,6 +1367,85 @@ __global__ __launch_bounds__(1024) void logits_reduce_finish_kernel(const float 
     }
 }
 
+// Low-M epilogue: store one finished 32-vocabulary-row block (AM x 32 masked rows) whose
+// first vocabulary row is vb; rows >= `rows` and vocabulary rows >= v_hi are not stored.
+// Lane (fr, hi) holds, per 16-entry group gq, vocabulary rows vb + 8 gq + 4 hi .. + 3 of
+// masked row bm * 32 + fr.
+template <int AM, bool OUT_BF16>
+__device__ __forceinline__ void lowm_store_block(const f32x16_t (&res)[AM], int vb, int v_hi, int rows, int fr,
+                                                 int hi, void *__restrict__ out, int64_t ldo)
+{
+#pragma unroll
+    for (int bm = 0; bm < AM; ++bm) {
+        const int row = bm * 32 + fr;
+        if (row >= rows)
+            continue;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int v = vb + gq * 8 + hi * 4;
+            const float x0 = res[bm][gq * 4 + 0], x1 = res[bm][gq * 4 + 1];
+            const float x2 = res[bm][gq * 4 + 2], x3 = res[bm][gq * 4 + 3];
+            const bool full = v + 3 < v_hi && (ldo & 3) == 0;
+            if constexpr (OUT_BF16) {
+                __bf16 *o = (__bf16 *)out + (int64_t)row * ldo + v;
+                if (full) {
+                    uint2 p;
+                    p.x = pack_bf16x2(x0, x1);
+                    p.y = pack_bf16x2(x2, x3);
+                    *(uint2 *)o = p;
+                } else {
+                    if (v + 0 < v_hi) o[0] = static_cast<__bf16>(x0);
+                    if (v + 1 < v_hi) o[1] = static_cast<__bf16>(x1);
+                    if (v + 2 < v_hi) o[2] = static_cast<__bf16>(x2);
+                    if (v + 3 < v_hi) o[3] = static_cast<__bf16>(x3);
+                }
+            } else {
+                float *o = (float *)out + (int64_t)row * ldo + v;
+                if (full) {
+                    *(f32x4_t *)o = f32x4_t{x0, x1, x2, x3};
+                } else {
+                    if (v + 0 < v_hi) o[0] = x0;
+                    if (v + 1 < v_hi) o[1] = x1;
+                    if (v + 2 < v_hi) o[2] = x2;
+                    if (v + 3 < v_hi) o[3] = x3;
+                }
+            }
+        }
+    }
+}
+
+// Low-M block results are held in registers, NBK blocks at most, and stored in one burst
+// when the wave's range ends or the registers are full.  Stores count in the same in-order
+// vmcnt as the DMA loads, so a store issued in the K loop would make the next K tile's wait
+// also wait for the store to be acknowledged by memory; holding the results keeps that
+// wait out of the stream.  `held` is oldest first; block blk has just finished into acc.
+template <int AM, int NBK, bool OUT_BF16>
+__device__ __forceinline__ void lowm_block_done(f32x16_t (&held)[NBK][AM], f32x16_t (&acc)[AM], int blk,
+                                                int nblocks, int v_lo, int v_hi, int rows, int fr, int hi,
+                                                void *__restrict__ out, int64_t ldo)
+{
+#pragma unroll
+    for (int i = 0; i + 1 < NBK; ++i)
+#pragma unroll
+        for (int bm = 0; bm < AM; ++bm)
+            held[i][bm] = held[i + 1][bm];
+#pragma unroll
+    for (int bm = 0; bm < AM; ++bm) {
+        held[NBK - 1][bm] = acc[bm];
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            acc[bm][e] = 0.0f;
+    }
+    const int n = blk % NBK + 1;   // blocks held since the last burst
+    if (n == NBK || blk == nblocks - 1) {
+#pragma unroll
+        for (int i = 0; i < NBK; ++i)
+            if (i >= NBK - n)
+                lowm_store_block<AM, OUT_BF16>(held[i], v_lo + (blk - (NBK - 1 - i)) * 32, v_hi, rows, fr, hi, out,
+                                               ldo);
+    }
+}
+
 // Low-M gather-GEMM (M <= 32 * AM): the work is streaming W once from HBM.
 //
 // Every wave is an independent stream.  Wave w of the grid owns an equal, contiguous
@@ -1385,6 +1464,7 @@ gather_gemm_lowm_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict_
                         int64_t ldo)
 {
     constexpr int BK = 64, ROW_BYTES = 128, CHUNKS = 8, RPI = 8;
+    constexpr int NBK = 8;                        // finished blocks held before a store burst
     constexpr int W_TILE = 32 * ROW_BYTES;        // 4 KiB: the wave's 32 rows
     constexpr int H_TILE = 32 * AM * ROW_BYTES;   // 4 or 8 KiB
     constexpr int STAGE = W_TILE + H_TILE;
@@ -1451,7 +1531,7 @@ gather_gemm_lowm_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict_
     const int a_addr = fr * ROW_BYTES + lane_chunk;
     const int b_addr = W_TILE + fr * ROW_BYTES + lane_chunk;
 
-    f32x16_t acc[AM];
+    f32x16_t acc[AM], held[NBK][AM];
 #pragma unroll
     for (int bm = 0; bm < AM; ++bm)
 #pragma unroll
@@ -1483,50 +1563,141 @@ gather_gemm_lowm_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict_
         rd = (rd + STAGE == WAVE_LDS) ? 0 : rd + STAGE;
 
         const int blk = g / nk;
-        if (g - blk * nk == nk - 1) {
-            // block done: store its outputs and restart the accumulation
-            const int vb = v_lo + blk * 32;
+        if (g - blk * nk == nk - 1)
+            lowm_block_done<AM, NBK, OUT_BF16>(held, acc, blk, nblocks, v_lo, v_hi, rows, fr, hi, out, ldo);
+    }
+}
+
+// At most n (0 <= n <= MAXN) DMA tiles of T instructions each still in flight.
+template <int T, int MAXN>
+__device__ __forceinline__ void wait_tiles_upto(int n)
+{
+    if constexpr (MAXN <= 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (n >= MAXN)
+            wait_vmcnt<MAXN * T>();
+        else
+            wait_tiles_upto<T, MAXN - 1>(n);
+    }
+}
+
+// Low-M gather-GEMM with the H tile shared by the workgroup (M <= 32 * AM).
+//
+// The W stream is as in gather_gemm_lowm_kernel: wave w of the grid owns an equal,
+// contiguous range of vocabulary rows and walks it in 32-row blocks, each a full K loop,
+// through a private LDS ring.  Here every wave of the grid runs the same number of
+// (block, K tile) steps (waves whose range is short run padding blocks of clamped rows
+// that are never stored), so the four waves of a workgroup need the same H tile at the
+// same step.  That tile (32 * AM masked rows x 64 k) is fetched once per workgroup into a
+// shared ring, each wave DMAing AM of its 8-row slices, and one barrier per step makes it
+// visible.  Against a per-wave H copy this reads H from L2 four times less and leaves the
+// LDS to a deeper W ring (8 stages for AM = 1: seven 4 KiB W tiles in flight per wave
+// while one is consumed).  The barrier also tells each wave that every other wave has
+// finished reading the previous step's slot, which is then refilled.
+// Same MFMA, operand roles and k order as the tiled kernel: results are bit-identical.
+template <int AM, int NSTAGE, bool OUT_BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
+gather_gemm_lowm_shared_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict__ idx, int32_t rows,
+                               const __bf16 *__restrict__ W, int32_t V, int32_t d, void *__restrict__ out,
+                               int64_t ldo)
+{
+    constexpr int BK = 64, ROW_BYTES = 128, CHUNKS = 8, RPI = 8;
+    constexpr int NBK = 8;                        // finished blocks held before a store burst
+    constexpr int W_TILE = 32 * ROW_BYTES;        // 4 KiB: a wave's 32 vocabulary rows
+    constexpr int H_TILE = 32 * AM * ROW_BYTES;   // 4 or 8 KiB, shared by the workgroup
+    constexpr int WAVE_W = NSTAGE * W_TILE;
+    constexpr int H_BASE = 4 * WAVE_W;
+    constexpr int LW = W_TILE / 1024;             // W DMA instructions per wave per step
+    constexpr int LH = AM;                        // H DMA instructions per wave per step
+    constexpr int T = LW + LH;
+    static_assert(H_BASE + NSTAGE * H_TILE <= 160 * 1024, "LDS");
+    static_assert(NSTAGE >= 3 && (NSTAGE - 2) * T < 64, "vmcnt");
+
+    __shared__ __attribute__((aligned(1024))) char smem[H_BASE + NSTAGE * H_TILE];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wbase = wave * WAVE_W;
+    const int64_t nw = (int64_t)gridDim.x * 4, gw = (int64_t)blockIdx.x * 4 + wave;
+    const int v_lo = (int)((gw * V) / nw);
+    const int v_hi = (int)(((gw + 1) * V) / nw);
+    const int v_max = max(v_hi - 1, 0);           // clamp for padding rows (V >= 1)
+    // every range is at most ceil(V / nw) rows: the same block count for all waves
+    const int nblocks = (int)(((V + nw - 1) / nw + 31) / 32);
+    const int nk = d / BK;
+    const int ntiles = nblocks * nk;
+
+    // DMA lanes: an instruction fills 8 tile rows (lane / 8) x 8 physical chunks (lane % 8).
+    int wch[LW];
 #pragma unroll
-            for (int bm = 0; bm < AM; ++bm) {
-                const int row = bm * 32 + fr;
-                if (row < rows) {
+    for (int j = 0; j < LW; ++j)
+        wch[j] = ((lane % CHUNKS) ^ swz<BK>(j * RPI + lane / CHUNKS)) * 16;
+    // H slice q = j * 4 + wave holds masked rows 8q .. 8q + 7 of the tile
+    const char *hsrc[LH];
 #pragma unroll
-                    for (int gq = 0; gq < 4; ++gq) {
-                        const int v = vb + gq * 8 + hi * 4;
-                        const float x0 = acc[bm][gq * 4 + 0], x1 = acc[bm][gq * 4 + 1];
-                        const float x2 = acc[bm][gq * 4 + 2], x3 = acc[bm][gq * 4 + 3];
-                        const bool full = v + 3 < v_hi && (ldo & 3) == 0;
-                        if constexpr (OUT_BF16) {
-                            __bf16 *o = (__bf16 *)out + (int64_t)row * ldo + v;
-                            if (full) {
-                                uint2 p;
-                                p.x = pack_bf16x2(x0, x1);
-                                p.y = pack_bf16x2(x2, x3);
-                                *(uint2 *)o = p;
-                            } else {
-                                if (v + 0 < v_hi) o[0] = static_cast<__bf16>(x0);
-                                if (v + 1 < v_hi) o[1] = static_cast<__bf16>(x1);
-                                if (v + 2 < v_hi) o[2] = static_cast<__bf16>(x2);
-                                if (v + 3 < v_hi) o[3] = static_cast<__bf16>(x3);
-                            }
-                        } else {
-                            float *o = (float *)out + (int64_t)row * ldo + v;
-                            if (full) {
-                                *(f32x4_t *)o = f32x4_t{x0, x1, x2, x3};
-                            } else {
-                                if (v + 0 < v_hi) o[0] = x0;
-                                if (v + 1 < v_hi) o[1] = x1;
-                                if (v + 2 < v_hi) o[2] = x2;
-                                if (v + 3 < v_hi) o[3] = x3;
-                            }
-                        }
-                    }
-                }
+    for (int j = 0; j < LH; ++j) {
+        const int r = (j * 4 + wave) * RPI + lane / CHUNKS;
+        hsrc[j] = (const char *)(H + (int64_t)idx[min(r, rows - 1)] * d) + ((lane % CHUNKS) ^ swz<BK>(r)) * 16;
+    }
+
+    auto issue = [&](int slot, int g) {
+        const int blk = g / nk, kt = g - blk * nk;
+        const int kb = kt * ROW_BYTES;
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    acc[bm][e] = 0.0f;
-            }
+        for (int j = 0; j < LW; ++j) {
+            const int v = min(v_lo + blk * 32 + j * RPI + lane / CHUNKS, v_max);
+            __builtin_amdgcn_global_load_lds((const void *)((const char *)(W + (int64_t)v * d) + kb + wch[j]),
+                                             (lds_void_t *)(smem + wbase + slot * W_TILE + j * 1024), 16, 0, 0);
         }
+#pragma unroll
+        for (int j = 0; j < LH; ++j)
+            __builtin_amdgcn_global_load_lds((const void *)(hsrc[j] + kb),
+                                             (lds_void_t *)(smem + H_BASE + slot * H_TILE + (j * 4 + wave) * 1024),
+                                             16, 0, 0);
+    };
+
+    const int fr = lane & 31, hi = lane >> 5;
+    const int lane_chunk = (hi ^ swz<BK>(fr)) * 16;
+    const int a_addr = wbase + fr * ROW_BYTES + lane_chunk;
+    const int b_addr = H_BASE + fr * ROW_BYTES + lane_chunk;
+
+    f32x16_t acc[AM], held[NBK][AM];
+#pragma unroll
+    for (int bm = 0; bm < AM; ++bm)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            acc[bm][e] = 0.0f;
+
+    // NSTAGE - 1 steps ahead; the last slot is filled once the first step's barrier has
+    // passed
+    const int npre = min(NSTAGE - 1, ntiles);
+    for (int g = 0; g < npre; ++g)
+        issue(g, g);
+
+    int rs = 0;   // slot of step g
+    for (int g = 0; g < ntiles; ++g) {
+        // this wave's part of step g has landed (younger: steps g+1 .. g+NSTAGE-2)
+        wait_tiles_upto<T, NSTAGE - 2>(min(NSTAGE - 2, ntiles - 1 - g));
+        barrier_no_fence();   // every wave's part landed; every wave is done with step g-1
+        if (g + NSTAGE - 1 < ntiles)
+            issue(rs == 0 ? NSTAGE - 1 : rs - 1, g + NSTAGE - 1);
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
+            const bf16x8_t af = *(const bf16x8_t *)(smem + ((a_addr + rs * W_TILE) ^ (32 * s)));
+            bf16x8_t bf[AM];
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm)
+                bf[bm] = *(const bf16x8_t *)(smem + ((b_addr + rs * H_TILE + bm * 32 * ROW_BYTES) ^ (32 * s)));
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm)
+                acc[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[bm], acc[bm], 0, 0, 0);
+        }
+        rs = (rs + 1 == NSTAGE) ? 0 : rs + 1;
+
+        const int blk = g / nk;
+        if (g - blk * nk == nk - 1)
+            lowm_block_done<AM, NBK, OUT_BF16>(held, acc, blk, nblocks, v_lo, v_hi, rows, fr, hi, out, ldo);
     }
 }
 
@@ -1728,6 +1899,25 @@ hipError_t launch_lowm(const void *H, const int32_t *idx, int64_t rows, const vo
     return hipGetLastError();
 }
 
+template <int AM>
+hipError_t launch_lowm_shared(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V, int64_t d,
+                              void *out, int64_t ldo, bool out_bf16, hipStream_t stream)
+{
+    constexpr int NSTAGE = AM == 1 ? 8 : 6;   // 160 / 144 KiB of LDS
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    // one workgroup (four streams) per CU, but never fewer than 32 rows per stream
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cus, (V + 127) / 128));
+    if (out_bf16)
+        hipLaunchKernelGGL((gather_gemm_lowm_shared_kernel<AM, NSTAGE, true>), dim3(grid), dim3(256), 0, stream,
+                           (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d, out, ldo);
+    else
+        hipLaunchKernelGGL((gather_gemm_lowm_shared_kernel<AM, NSTAGE, false>), dim3(grid), dim3(256), 0, stream,
+                           (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d, out, ldo);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V)
@@ -1755,6 +1945,7 @@ bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V)
     case kVariantBf16M16S1:
         return ((rows + 255) / 256) * ((V + 255) / 256) <= 0x7fffffffLL;
     case kVariantBf16LowM:
+    case kVariantBf16LowMShared:
         return rows <= 64;
     default:
         return false;
@@ -1849,6 +2040,10 @@ hipError_t launch_gather_gemm(int variant, const void *H, const int32_t *idx, in
         if (rows <= 32)
             return launch_lowm<1>(H, idx, rows, W, V, d, out, ldo, out_bf16, stream);
         return launch_lowm<2>(H, idx, rows, W, V, d, out, ldo, out_bf16, stream);
+    case kVariantBf16LowMShared:
+        if (rows <= 32)
+            return launch_lowm_shared<1>(H, idx, rows, W, V, d, out, ldo, out_bf16, stream);
+        return launch_lowm_shared<2>(H, idx, rows, W, V, d, out, ldo, out_bf16, stream);
     default:
         return hipErrorInvalidValue;
     }

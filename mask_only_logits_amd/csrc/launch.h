@@ -38,7 +38,8 @@ enum LogitsVariant : int {
     kVariantBf16DeferS16 = 17,     // ... stores spread over 16 K steps
     kVariantBf16M16 = 18,          // persistent 8-wave, 16 x 16 x 32 MFMA, bf16 out, stores at each tile's end
     kVariantBf16M16S1 = 19,        // ... refill DMA in one k sub-step (the bf16-output default)
-    kNumVariants = 20,
+    kVariantBf16LowMShared = 20,   // bf16, d % 64 == 0, M <= 64: W streaming with a workgroup-shared H tile
+    kNumVariants = 21,
 };
 
 // Default number of row tiles that share the W slabs of one XCD (tile order).

@@ -126,7 +126,8 @@ bool variant_can_run(int v, int64_t M, int64_t d, mosaic_dtype_t in, mosaic_dtyp
     case mosaic::kVariantBf16K32S3:
     case mosaic::kVariantBf16K32S4:
     case mosaic::kVariantBf16K32S5: return bf16_in && d % 32 == 0 && small_d;
-    case mosaic::kVariantBf16LowM: return bf16_in && d % 64 == 0 && small_d && M <= 64;
+    case mosaic::kVariantBf16LowM:
+    case mosaic::kVariantBf16LowMShared: return bf16_in && d % 64 == 0 && small_d && M <= 64;
     default: return false;
     }
 }
@@ -141,8 +142,8 @@ int pick_variant(int64_t M, int64_t V, int64_t d, mosaic_dtype_t in, mosaic_dtyp
         return mosaic::kVariantF32;
     // Every bf16 variant below for one d accumulates each output in the same MFMA k
     // order, so the choice (made per launch from its row count) never changes a bit.
-    if (variant_can_run(mosaic::kVariantBf16LowM, M, d, in, out))
-        return mosaic::kVariantBf16LowM;
+    if (variant_can_run(mosaic::kVariantBf16LowMShared, M, d, in, out))
+        return mosaic::kVariantBf16LowMShared;
     if (variant_can_run(mosaic::kVariantBf16M16S1, M, d, in, out))
         return mosaic::kVariantBf16M16S1;
     if (variant_can_run(mosaic::kVariantBf16W8K64S2, M, d, in, out))
@@ -262,7 +263,7 @@ mosaic_status_t mosaic_masked_logits(const void *H, int64_t L, int64_t d, const 
         return MOSAIC_ERR_UNSUPPORTED;
     const int v_full = pick_variant(C, V, d, in_dtype, out_dtype);
     int v_tail = pick_variant(tail, V, d, in_dtype, out_dtype);
-    if (v_tail != mosaic::kVariantBf16LowM)
+    if (v_tail != mosaic::kVariantBf16LowM && v_tail != mosaic::kVariantBf16LowMShared)
         v_tail = v_full;
     if (v_full < 0 || v_tail < 0 || !mosaic::gather_gemm_grid_fits(v_full, C, V) ||
         !mosaic::gather_gemm_grid_fits(v_tail, tail, V))

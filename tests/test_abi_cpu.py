@@ -60,8 +60,8 @@ def test_variant_choice(m):
     assert m.mosaic_logits_variant(4096, 126464, 4096, bf, bf) == 19     # persistent, 16 x 16 x 32 MFMA
     assert m.mosaic_logits_variant(65, 152064, 3584, bf, bf) == 19
     assert m.mosaic_logits_variant(4096, 126464, 4096, bf, f32) == 12    # 8-wave tiled kernel
-    assert m.mosaic_logits_variant(20, 152064, 3584, bf, bf) == 6        # low-M streaming kernel
-    assert m.mosaic_logits_variant(64, 152064, 3584, bf, f32) == 6
+    assert m.mosaic_logits_variant(20, 152064, 3584, bf, bf) == 20       # low-M streaming kernel, shared H
+    assert m.mosaic_logits_variant(64, 152064, 3584, bf, f32) == 20
     assert m.mosaic_logits_variant(20, 1000, 96, bf, bf) == 11           # d % 32 == 0 only
     assert m.mosaic_logits_variant(5000, 1000, 96, bf, f32) == 11
     assert m.mosaic_logits_variant(128, 1024, 256, f32, f32) == 0

@@ -70,12 +70,20 @@ LOWM_CASES = [
     ("bf16", 300, 192, 1001, 31), ("bf16", 300, 256, 777, 32), ("bf16", 300, 256, 4097, 33),
     ("bf16", 300, 512, 300, 63), ("bf16", 300, 512, 2000, 64), ("f32", 300, 256, 1031, 17),
     ("f32", 300, 320, 515, 50),
+    # several 32-row blocks per wave; at V = 131584 the 1024 waves own 128 or 129 rows, so
+    # the shorter ones run a padding block
+    ("bf16", 300, 64, 131584, 20), ("bf16", 300, 128, 131584, 40), ("f32", 300, 64, 40000, 64),
+    # more than 8 blocks per wave: the held results go out in two bursts
+    ("bf16", 300, 64, 300000, 20), ("f32", 300, 64, 300000, 40),
 ]
 
 
+@pytest.mark.parametrize("variant", [6, 20])
 @pytest.mark.parametrize("dt_out,L,d,V,M", LOWM_CASES)
-def test_parity_lowm(m, dt_out, L, d, V, M):
-    assert m.mosaic_logits_variant(M, V, d, torch.bfloat16, TD[dt_out]) == 6
+def test_parity_lowm(m, monkeypatch, variant, dt_out, L, d, V, M):
+    # both low-M streaming kernels: private H copies per wave (6) and a workgroup-shared H tile (20)
+    monkeypatch.setenv("MOSAIC_TUNE", f"variant={variant}")
+    assert m.mosaic_logits_variant(M, V, d, torch.bfloat16, TD[dt_out]) == variant
     wl = inputs.make_random(L + d + V + M, L=L, d=d, V=V, M=M, dtype="bf16")
     idx, idx_d = _gpu_idx(wl)
     out = m.mosaic_masked_logits(wl.H.to(DEV), idx_d, wl.W.to(DEV), out_dtype=TD[dt_out])
@@ -88,17 +96,19 @@ def test_parity_lowm(m, dt_out, L, d, V, M):
                                        (600, 64, 70000, "bf16"), (600, 1280, 70000, "bf16"),
                                        # whole tiles (rows and V multiples of 256), several per workgroup
                                        (1024, 512, 65536, "bf16"), (1024, 64, 65536, "bf16"),
-                                       (2048, 128, 32768, "bf16")])
+                                       (2048, 128, 32768, "bf16"),
+                                       # low-M shapes with several blocks per wave
+                                       (20, 64, 131584, "bf16"), (64, 128, 40000, "f32"), (20, 64, 300000, "bf16")])
 def test_bf16_variants_bit_identical(m, monkeypatch, M, d, V, out):
     # every bf16 MFMA variant accumulates each output in the same MFMA k order
     wl = inputs.make_random(M + d + V, L=max(M, 300), d=d, V=V, M=M, dtype="bf16")
     _, idx_d = _gpu_idx(wl)
     H, W = wl.H.to(DEV), wl.W.to(DEV)
     ref = m.mosaic_masked_logits(H, idx_d, W, out_dtype=TD[out])
-    for v in range(1, 20):
+    for v in range(1, 21):
         if v == 2:
             continue
-        if v == 6 and M > 64:
+        if v in (6, 20) and M > 64:
             continue
         monkeypatch.setenv("MOSAIC_TUNE", f"variant={v}")
         if out == "bf16" or v < 15:            # the deferred-store kernels write bf16 only
