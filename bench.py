@@ -60,11 +60,14 @@ def code_lines(text: str):
     return out
 
 
-def kernel_source_hash() -> str:
-    """Hash of the gather-GEMM sources' code lines, so that a measured traffic figure
-    stays attached to the code it was measured on (comment edits keep it)."""
+def kernel_source_hash(path: str = "logits") -> str:
+    """Hash of the code lines of the sources the path's kernels are built from, so that a
+    measured traffic figure stays attached to the code it was measured on (comment edits
+    keep it): the FP8 kernels for the fp8 path, the bf16/fp32 kernels for the others,
+    and the C ABI and launcher header for all."""
     h = hashlib.sha256()
-    for f in ("gather_gemm.hip", "gather_gemm_fp8.hip", "mosaic_abi.cpp", "launch.h"):
+    kernels = "gather_gemm_fp8.hip" if path == "fp8" else "gather_gemm.hip"
+    for f in (kernels, "mosaic_abi.cpp", "launch.h"):
         with open(os.path.join(ROOT, "mask_only_logits_amd", "csrc", f), encoding="utf-8") as fh:
             for line in code_lines(fh.read()):
                 h.update(line.encode() + b"\n")
@@ -85,7 +88,7 @@ def measured_traffic(workload: str, path: str = "logits", prof_dir: str | None =
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(path):
         return None
     return t.get("bytes_per_launch")
 
@@ -190,7 +193,7 @@ def summarize_profile(root: str, workload: str, copy_mib: int, path: str = "logi
         w_scale = known / (sum(cp["WRITE_SIZE"]) / len(cp["WRITE_SIZE"]) * 1024)
         fetch = sum(g["FETCH_SIZE"]) / len(g["FETCH_SIZE"]) * 1024 * f_scale
         write = sum(g["WRITE_SIZE"]) / len(g["WRITE_SIZE"]) * 1024 * w_scale
-        traffic = {"kernel_source_hash": kernel_source_hash(), "workload": workload, "path": path,
+        traffic = {"kernel_source_hash": kernel_source_hash(path), "workload": workload, "path": path,
                    "bytes_per_launch": int(fetch + write), "fetch_bytes_per_launch": int(fetch),
                    "write_bytes_per_launch": int(write), "fetch_scale": f_scale, "write_scale": w_scale,
                    "copy_probe_bytes": known}

@@ -145,7 +145,12 @@ gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__
     constexpr int NDMA = LW + LH, PER = NDMA / NSPREAD;
     static_assert(NDMA % NSPREAD == 0 && NSPREAD <= NSUB, "spread");
 
-    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+    // The stages, then the tile's row scales: 256 of W, then 256 of H (fp32).  One
+    // allocation: with a second __shared__ array the compiler cannot tell the stage DMA
+    // from the fragment reads and waits for the DMA before every read.
+    constexpr int SC_BASE = NSTAGE * STAGE;
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE + 2 * BV * 4];
+    static_assert(BV == BM, "scale staging assumes square tiles");
 
     const int nvt = (V + BV - 1) / BV;
     const int nmt = (rows + BM - 1) / BM;
@@ -298,6 +303,14 @@ gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__
     // read is split over the last sub-step of a step and the first of the next).
     const int nk = d / BK;
     i32x8_t af[2][AV], bf[2][AM];
+    // The epilogue's row scales reach LDS by DMA ahead of the K loop (8 instructions of
+    // 64 x 4 bytes: W scales v0 .. v0+255, then H scales m0 .. m0+255, indices clamped to
+    // the last valid row, whose copies are never used), so the epilogue issues no global
+    // loads.  They are older than the first stage's DMA, so the first wait covers them.
+    for (int j = wave; j < 8; j += NW) {
+        const float *src = j < 4 ? ws + min(v0 + j * 64 + lane, V - 1) : hs + min(m0 + (j - 4) * 64 + lane, rows - 1);
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_t *)(smem + SC_BASE + j * 256), 4, 0, 0);
+    }
     const int npre = min(NSTAGE, nk);
     for (int s = 0; s < npre; ++s)
 #pragma unroll
@@ -365,11 +378,12 @@ gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__
     };
     {
         const bool vec_ok = ((uintptr_t)out & 15) == 0 && (ldo & 7) == 0;
+        const float *sc = (const float *)(smem + SC_BASE);
 #pragma unroll
         for (int bm = 0; bm < AM; ++bm) {
             const int row = m0 + wm * WM + bm * 32 + fr;
             const bool row_ok = row < rows;
-            const float h = hs[min(row, rows - 1)];
+            const float h = sc[BV + wm * WM + bm * 32 + fr];
 #pragma unroll
             for (int a = 0; a < AV; ++a) {
                 const int vb = v0 + wv * WV + a * 32;
@@ -377,17 +391,7 @@ gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
                     const int v = vb + gq * 8 + hi * 4;
-                    float w[4];
-                    if (v + 3 < V) {
-                        const f32x4_t w4 = *(const f32x4_t *)(ws + v);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            w[e] = w4[e];
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            w[e] = ws[min(v + e, V - 1)];
-                    }
+                    const f32x4_t w = *(const f32x4_t *)(sc + (v - v0));
                     pk[gq][0] = pack2(acc[a][bm][gq * 4 + 0] * (h * w[0]), acc[a][bm][gq * 4 + 1] * (h * w[1]));
                     pk[gq][1] = pack2(acc[a][bm][gq * 4 + 2] * (h * w[2]), acc[a][bm][gq * 4 + 3] * (h * w[3]));
                 }

@@ -69,6 +69,13 @@ def test_summarize_profile_scales_by_the_copy_probe(tmp_path):
     assert bench.measured_traffic("absent", "logits", prof_dir=str(prof)) is None
 
 
+def test_source_hash_follows_the_paths_kernels():
+    # the fp8 path's figures hang on the FP8 kernels' source, the others' on the bf16 kernels'
+    assert bench.kernel_source_hash("argmax_lse") == bench.kernel_source_hash("logits")
+    assert bench.kernel_source_hash("dense_select") == bench.kernel_source_hash("logits")
+    assert bench.kernel_source_hash("fp8") != bench.kernel_source_hash("logits")
+
+
 def test_no_traffic_without_both_counters(tmp_path):
     raw, prof = tmp_path / "raw", tmp_path / "prof"
     _write_csv(str(raw / "fetch" / "fetch_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
