@@ -126,6 +126,27 @@ def cpu_baseline(wl, idx_np, target_s: float, path: str = "logits"):
                       f"{dt:.1f} s"}
 
 
+def cpu_per_core(wl, idx_np, path: str = "logits"):
+    """The oracle on one thread over one masked row: the per-core rate beside the all-core
+    cpu_baseline."""
+    import oracle
+    cores = oracle.num_threads()
+    fn = oracle.masked_logits if path == "logits" else oracle.masked_logits_argmax_lse
+    oracle.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        fn(wl.H, idx_np, wl.W, rows=[0])
+        t1 = max(1e-4, time.perf_counter() - t0)
+        n = int(max(1, min(len(idx_np), 0.5 / t1)))   # about half a second of one core
+        t0 = time.perf_counter()
+        fn(wl.H, idx_np, wl.W, rows=list(range(n)))
+        dt = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": round(n * 2.0 * wl.d * wl.V / dt / 1e12, 6), "unit": "TFLOP/s", "threads": 1,
+            "sample": f"{n} masked rows x all {wl.V} vocabulary rows, {dt:.2f} s"}
+
+
 def _read_csv(path):
     import csv
     with open(path, newline="", encoding="utf-8") as fh:
@@ -462,6 +483,7 @@ def main():
         idx_np = idx[:M].cpu().numpy()
         log("[bench] timing the CPU oracle on a row sample ...")
         result["cpu_baseline"] = cpu_baseline(wl, idx_np, args.cpu_seconds, args.path)
+        result["detail"]["cpu_per_core"] = cpu_per_core(wl, idx_np, args.path)
         result["detail"]["host"] = host_info()
         log(f"[bench] cpu_baseline {result['cpu_baseline']}")
     else:

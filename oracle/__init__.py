@@ -79,6 +79,8 @@ def _load():
         lib.oracle_logits_bytes.argtypes = [_i64, _i64, _i64]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_set_num_threads.restype = None
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -107,6 +109,11 @@ def _ptr(a: np.ndarray):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's later parallel loops (OpenMP), n >= 1."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def logits_bytes(rows: int, V: int, esize: int) -> int:

@@ -416,8 +416,11 @@ int oracle_logits_fp8(const uint8_t *qh, const float *scale_h, int64_t M, const 
 #ifdef _OPENMP
 #include <omp.h>
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+/* Threads of the later parallel loops of the calling thread (n >= 1). */
+void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int oracle_num_threads(void) { return 1; }
+void oracle_set_num_threads(int n) { (void)n; }
 #endif
 
 /* Bytes of a logits tensor of `rows` rows over a vocabulary of V entries with

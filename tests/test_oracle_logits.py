@@ -128,3 +128,19 @@ def test_out_of_range_index_is_an_error():
         oracle.masked_logits(wl.H, np.array([0, 10], np.int32), wl.W)
     with pytest.raises(IndexError):
         oracle.masked_logits(wl.H, np.array([0, 1], np.int32), wl.W, rows=np.array([2]))
+
+
+def test_thread_count_does_not_change_results():
+    # each logit is one ascending-k sum on one thread, so the thread count cannot matter
+    wl = inputs.make_random(77, L=300, d=128, V=500, M=150, dtype="bf16")
+    idx = oracle.mask_compact(wl.tokens, wl.mask_id)
+    n = oracle.num_threads()
+    ref = oracle.masked_logits(wl.H, idx, wl.W)
+    oracle.set_num_threads(1)
+    try:
+        assert oracle.num_threads() == 1
+        one = oracle.masked_logits(wl.H, idx, wl.W)
+    finally:
+        oracle.set_num_threads(n)
+    assert oracle.num_threads() == n
+    assert np.array_equal(one, ref)
