@@ -1369,8 +1369,8 @@ __global__ __launch_bounds__(1024) void logits_reduce_finish_kernel(const float 
 
 // Low-M epilogue: store one finished 32-vocabulary-row block (AM x 32 masked rows) whose
 // first vocabulary row is vb; rows >= `rows` and vocabulary rows >= v_hi are not stored.
-// Lane (fr, hi) holds, per 16-entry group gq, vocabulary rows vb + 8 gq + 4 hi .. + 3 of
-// masked row bm * 32 + fr.
+// Lane (fr, hi) holds, in accumulators 4 gq .. 4 gq + 3 of block bm, vocabulary rows
+// vb + 8 gq + 4 hi .. + 3 of masked row bm * 32 + fr.
 template <int AM, bool OUT_BF16>
 __device__ __forceinline__ void lowm_store_block(const f32x16_t (&res)[AM], int vb, int v_hi, int rows, int fr,
                                                  int hi, void *__restrict__ out, int64_t ldo)
