@@ -119,3 +119,33 @@ def test_integer_inputs_full_shape_bit_exact(m):
     rows = sample_rows(want.size, 0, 6, seed=5)
     ref = oracle.masked_logits(H, want, W, rows=rows)
     assert torch.equal(out[torch.from_numpy(rows).to(DEV)].cpu(), bf16_rne(ref))
+
+
+@pytest.mark.parametrize("M", [33, 64])
+def test_lowm_shape_two_row_blocks_every_element(m, M):
+    # the low-M workload's H and W (d = 3584, V = 152064) with 33 and 64 masked rows: the
+    # low-M kernel's two-row-block form across the full grid, bf16 and fp32 logits, every
+    # element against the oracle
+    wl = inputs.make_workload("lowm")
+    idx = np.sort(np.random.default_rng(M).choice(wl.L, M, replace=False)).astype(np.int32)
+    H, W, idx_d = wl.H.to(DEV), wl.W.to(DEV), torch.from_numpy(idx).to(DEV)
+    assert m.mosaic_logits_variant(M, wl.V, wl.d, torch.bfloat16, torch.bfloat16) == 20
+    out16 = m.mosaic_masked_logits(H, idx_d, W)
+    out32 = m.mosaic_masked_logits(H, idx_d, W, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.masked_logits(wl.H, idx, wl.W)
+    assert_close(out16, ref, f"lowm shape M={M} bf16")
+    assert_close(out32, ref, f"lowm shape M={M} fp32")
+
+
+def test_chunk_tail_on_lowm_kernel_bit_exact(m):
+    # 1200-row chunks of the LLaDA-shaped step leave a 29-row tail, which runs on the low-M
+    # kernel while the first chunk runs on the tiled kernel: still bit-identical to the
+    # unchunked call
+    wl = inputs.make_workload("llada_step")
+    H, W, idx, M, out = _step(m, wl)
+    assert M == 1229 and m.mosaic_num_chunks(M, 1200) == 2
+    assert m.mosaic_logits_variant(M - 1200, wl.V, wl.d, torch.bfloat16, torch.bfloat16) == 20
+    chunked = m.mosaic_masked_logits(H, idx, W, M=M, chunk_rows=1200)
+    torch.cuda.synchronize()
+    assert torch.equal(chunked, out)
