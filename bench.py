@@ -67,7 +67,7 @@ def kernel_source_hash(path: str = "logits") -> str:
     and the C ABI and launcher header for all."""
     h = hashlib.sha256()
     kernels = "gather_gemm_fp8.hip" if path == "fp8" else "gather_gemm.hip"
-    for f in (kernels, "mosaic_abi.cpp", "launch.h"):
+    for f in (kernels, "lowm_epilogue.h", "mosaic_abi.cpp", "launch.h"):
         with open(os.path.join(ROOT, "mask_only_logits_amd", "csrc", f), encoding="utf-8") as fh:
             for line in code_lines(fh.read()):
                 h.update(line.encode() + b"\n")
@@ -400,12 +400,13 @@ def main():
         # the dense baseline's own work: all L rows
         alg_bytes = launches * V * d * esize_in + L * d * esize_in + (L + 2 * M) * V * out.element_size()
     traffic = measured_traffic(args.workload, args.path)
-    kernel = "gather_gemm_fp8_kernel" if fp8 else "gather_gemm_bf16_defer_kernel" if consumer else {0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel", 6: "gather_gemm_lowm_kernel", 20: "gather_gemm_lowm_shared_kernel",
+    fp8_lowm = fp8 and rows_per_launch <= 64 and "fp8lowm=0" not in os.environ.get("MOSAIC_TUNE", "")
+    kernel = ("gather_gemm_fp8_lowm_kernel" if fp8_lowm else "gather_gemm_fp8_kernel") if fp8 else "gather_gemm_bf16_defer_kernel" if consumer else {0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel", 6: "gather_gemm_lowm_kernel", 20: "gather_gemm_lowm_shared_kernel",
               9: "gather_gemm_bf16_persist_kernel", 10: "gather_gemm_bf16_persist_kernel",
               11: "gather_gemm_bf16_persist_kernel", 15: "gather_gemm_bf16_defer_kernel",
               16: "gather_gemm_bf16_defer_kernel", 17: "gather_gemm_bf16_defer_kernel",
               18: "gather_gemm_bf16_defer_kernel", 19: "gather_gemm_bf16_defer_kernel"}.get(variant, "gather_gemm_bf16_kernel")
-    if variant in LOWM_VARIANTS:
+    if variant in LOWM_VARIANTS or fp8_lowm:
         # streaming W is the bound: algorithmic bytes per launch over the launch time
         achieved_gbs = alg_bytes / launches / (gemm_avg / launches / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -442,7 +443,7 @@ def main():
                    "peak_logits_bytes": int((L * V + M * V) * out.element_size()) if dense else
                    (0 if consumer else int(M * V * out.element_size()))},
     }
-    flush_mib = args.flush_mib if args.flush_mib >= 0 else (512 if variant in LOWM_VARIANTS else 0)
+    flush_mib = args.flush_mib if args.flush_mib >= 0 else (512 if variant in LOWM_VARIANTS or fp8_lowm else 0)
     if flush_mib:
         # W no longer partly in the caches from the previous step: read a buffer larger than
         # the Infinity Cache before each step, outside the GEMM events (a read, so the flush
@@ -460,7 +461,7 @@ def main():
         fmed = float(np.median(fms))
         result["detail"]["flushed"] = {"flush_mib": flush_mib, "gemm_ms_median": round(fmed, 4),
                                        "gemm_ms_min": round(min(fms), 4)}
-        if variant in LOWM_VARIANTS:
+        if variant in LOWM_VARIANTS or fp8_lowm:
             result["detail"]["flushed"]["achieved_gbs"] = round(alg_bytes / (fmed / 1e3) / 1e9, 1)
         else:
             result["detail"]["flushed"]["achieved_tflops"] = round(flop / (fmed / 1e3) / 1e12, 2)

@@ -46,6 +46,7 @@
 #include <utility>
 
 #include "launch.h"
+#include "lowm_epilogue.h"
 
 namespace mosaic {
 namespace {
@@ -1373,85 +1374,6 @@ __global__ __launch_bounds__(1024) void logits_reduce_finish_kernel(const float 
 // (rocprofv3, one box), while H, which every step re-reads, keeps the default policy.
 constexpr int kLoadStreaming = 2;
 
-// Low-M epilogue: store one finished 32-vocabulary-row block (AM x 32 masked rows) whose
-// first vocabulary row is vb; rows >= `rows` and vocabulary rows >= v_hi are not stored.
-// Lane (fr, hi) holds, in accumulators 4 gq .. 4 gq + 3 of block bm, vocabulary rows
-// vb + 8 gq + 4 hi .. + 3 of masked row bm * 32 + fr.
-template <int AM, bool OUT_BF16>
-__device__ __forceinline__ void lowm_store_block(const f32x16_t (&res)[AM], int vb, int v_hi, int rows, int fr,
-                                                 int hi, void *__restrict__ out, int64_t ldo)
-{
-#pragma unroll
-    for (int bm = 0; bm < AM; ++bm) {
-        const int row = bm * 32 + fr;
-        if (row >= rows)
-            continue;
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            const int v = vb + gq * 8 + hi * 4;
-            const float x0 = res[bm][gq * 4 + 0], x1 = res[bm][gq * 4 + 1];
-            const float x2 = res[bm][gq * 4 + 2], x3 = res[bm][gq * 4 + 3];
-            const bool full = v + 3 < v_hi && (ldo & 3) == 0;
-            if constexpr (OUT_BF16) {
-                __bf16 *o = (__bf16 *)out + (int64_t)row * ldo + v;
-                if (full) {
-                    uint2 p;
-                    p.x = pack_bf16x2(x0, x1);
-                    p.y = pack_bf16x2(x2, x3);
-                    *(uint2 *)o = p;
-                } else {
-                    if (v + 0 < v_hi) o[0] = static_cast<__bf16>(x0);
-                    if (v + 1 < v_hi) o[1] = static_cast<__bf16>(x1);
-                    if (v + 2 < v_hi) o[2] = static_cast<__bf16>(x2);
-                    if (v + 3 < v_hi) o[3] = static_cast<__bf16>(x3);
-                }
-            } else {
-                float *o = (float *)out + (int64_t)row * ldo + v;
-                if (full) {
-                    *(f32x4_t *)o = f32x4_t{x0, x1, x2, x3};
-                } else {
-                    if (v + 0 < v_hi) o[0] = x0;
-                    if (v + 1 < v_hi) o[1] = x1;
-                    if (v + 2 < v_hi) o[2] = x2;
-                    if (v + 3 < v_hi) o[3] = x3;
-                }
-            }
-        }
-    }
-}
-
-// Low-M block results are held in registers, NBK blocks at most, and stored in one burst
-// when the wave's range ends or the registers are full.  Stores count in the same in-order
-// vmcnt as the DMA loads, so a store issued in the K loop would make the next K tile's wait
-// also wait for the store to be acknowledged by memory; holding the results keeps that
-// wait out of the stream.  `held` is oldest first; block blk has just finished into acc.
-template <int AM, int NBK, bool OUT_BF16>
-__device__ __forceinline__ void lowm_block_done(f32x16_t (&held)[NBK][AM], f32x16_t (&acc)[AM], int blk,
-                                                int nblocks, int v_lo, int v_hi, int rows, int fr, int hi,
-                                                void *__restrict__ out, int64_t ldo)
-{
-#pragma unroll
-    for (int i = 0; i + 1 < NBK; ++i)
-#pragma unroll
-        for (int bm = 0; bm < AM; ++bm)
-            held[i][bm] = held[i + 1][bm];
-#pragma unroll
-    for (int bm = 0; bm < AM; ++bm) {
-        held[NBK - 1][bm] = acc[bm];
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-            acc[bm][e] = 0.0f;
-    }
-    const int n = blk % NBK + 1;   // blocks held since the last burst
-    if (n == NBK || blk == nblocks - 1) {
-#pragma unroll
-        for (int i = 0; i < NBK; ++i)
-            if (i >= NBK - n)
-                lowm_store_block<AM, OUT_BF16>(held[i], v_lo + (blk - (NBK - 1 - i)) * 32, v_hi, rows, fr, hi, out,
-                                               ldo);
-    }
-}
-
 // Low-M gather-GEMM (M <= 32 * AM): the work is streaming W once from HBM.
 //
 // Every wave is an independent stream.  Wave w of the grid owns an equal, contiguous
@@ -1570,7 +1492,7 @@ gather_gemm_lowm_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict_
 
         const int blk = g / nk;
         if (g - blk * nk == nk - 1)
-            lowm_block_done<AM, NBK, OUT_BF16>(held, acc, blk, nblocks, v_lo, v_hi, rows, fr, hi, out, ldo);
+            lowm::lowm_block_done<AM, NBK, OUT_BF16>(held, acc, blk, nblocks, v_lo, v_hi, rows, fr, hi, out, ldo);
     }
 }
 
@@ -1710,7 +1632,7 @@ gather_gemm_lowm_shared_kernel(const __bf16 *__restrict__ H, const int32_t *__re
 
         const int blk = g / nk;
         if (g - blk * nk == nk - 1)
-            lowm_block_done<AM, NBK, OUT_BF16>(held, acc, blk, nblocks, v_lo, v_hi, rows, fr, hi, out, ldo);
+            lowm::lowm_block_done<AM, NBK, OUT_BF16>(held, acc, blk, nblocks, v_lo, v_hi, rows, fr, hi, out, ldo);
     }
 }
 

@@ -24,6 +24,7 @@
 #include <algorithm>
 
 #include "launch.h"
+#include "lowm_epilogue.h"
 
 namespace mosaic {
 namespace {
@@ -40,6 +41,20 @@ __device__ __forceinline__ void wait_vm()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0x0 << 8) | ((N >> 4) << 14));
+}
+
+// At most n (0 <= n <= MAXN) DMA tiles of T instructions each still in flight.
+template <int T, int MAXN>
+__device__ __forceinline__ void wait_tiles_upto_fp8(int n)
+{
+    if constexpr (MAXN <= 0) {
+        wait_vm<0>();
+    } else {
+        if (n >= MAXN)
+            wait_vm<MAXN * T>();
+        else
+            wait_tiles_upto_fp8<T, MAXN - 1>(n);
+    }
 }
 
 __device__ __forceinline__ void bar()
@@ -418,6 +433,164 @@ gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__
     }
 }
 
+
+// Low-M FP8 logits (rows <= 32 * AM): streaming the W codes once.
+// The bf16 low-M kernel's design with fp8 operands:
+//  * wave w of the grid owns an equal, contiguous range of vocabulary rows (the
+//    workgroups of one XCD a contiguous eighth), walked in 32-row blocks, each a full K
+//    loop of 128-code K tiles; 128-byte rows, so the DMA, the XOR swizzle and the per-wave
+//    LDS ring are the bf16 kernel's;
+//  * the 32 * AM quantized masked rows form an H tile shared by the workgroup (each wave
+//    DMAs AM 8-row slices), made visible by one barrier per step;
+//  * W's requests use the streaming cache policy (read once per launch);
+//  * each 64-code k sub-step is one v_mfma_scale_f32_32x32x64_f8f6f4 per block with the
+//    fragments and k order of gather_gemm_fp8_kernel, and the epilogue computes
+//    sum * (scale_h * scale_w) as it does, so the logits are bit-identical to it;
+//  * the row scales reach LDS by DMA (the H scales before the loop, a block's W scales
+//    one block ahead), so the K loop's waits count the stream alone;
+//  * a finished block's logits are held in registers and stored in bursts.
+template <int AM, int NSTAGE>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
+gather_gemm_fp8_lowm_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__ hs, int32_t rows,
+                            const uint8_t *__restrict__ Wq, const float *__restrict__ ws, int32_t V, int32_t d,
+                            __bf16 *__restrict__ out, int64_t ldo)
+{
+    constexpr int BK = 128, ROW_BYTES = 128, CHUNKS = 8, RPI = 8, NBK = 8;
+    constexpr int W_TILE = 32 * ROW_BYTES;           // 4 KiB: a wave's 32 vocabulary rows
+    constexpr int H_TILE = 32 * AM * ROW_BYTES;      // shared by the workgroup
+    constexpr int WAVE_W = NSTAGE * W_TILE;
+    constexpr int H_BASE = 4 * WAVE_W;
+    constexpr int SC_BASE = H_BASE + NSTAGE * H_TILE;
+    constexpr int SC_WAVE = 3 * 256;                 // per wave: 64 H scales, two slots of 64 W scales
+    constexpr int LW = W_TILE / 1024, LH = AM, T = LW + LH;
+    constexpr int kStream = 2;                       // global_load_lds cache policy: NT (streaming)
+    static_assert(SC_BASE + 4 * SC_WAVE <= 160 * 1024, "LDS");
+    static_assert(NSTAGE >= 3 && (NSTAGE - 2) * T < 64, "vmcnt");
+
+    __shared__ __attribute__((aligned(1024))) char smem[SC_BASE + 4 * SC_WAVE];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wbase = wave * WAVE_W;
+    const int sbase = SC_BASE + wave * SC_WAVE;
+    const int64_t wg = gridDim.x % 8 == 0 ? (int64_t)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8
+                                          : (int64_t)blockIdx.x;
+    const int64_t nw = (int64_t)gridDim.x * 4, gw = wg * 4 + wave;
+    const int v_lo = (int)((gw * V) / nw);
+    const int v_hi = (int)(((gw + 1) * V) / nw);
+    const int v_max = max(v_hi - 1, 0);              // clamp for padding rows (V >= 1)
+    const int nblocks = (int)(((V + nw - 1) / nw + 31) / 32);
+    const int nk = d / BK;
+    const int ntiles = nblocks * nk;
+    auto swz = [](int r) { return (r >> 1) & 7; };
+
+    int wch[LW];
+#pragma unroll
+    for (int j = 0; j < LW; ++j)
+        wch[j] = ((lane % CHUNKS) ^ swz(j * RPI + lane / CHUNKS)) * 16;
+    const uint8_t *hsrc[LH];
+#pragma unroll
+    for (int j = 0; j < LH; ++j) {
+        const int r = (j * 4 + wave) * RPI + lane / CHUNKS;
+        hsrc[j] = Hq + (int64_t)min(r, rows - 1) * d + ((lane % CHUNKS) ^ swz(r)) * 16;
+    }
+    auto issue = [&](int slot, int g) {
+        const int blk = g / nk, kt = g - blk * nk;
+        const int kb = kt * ROW_BYTES;
+#pragma unroll
+        for (int j = 0; j < LW; ++j) {
+            const int v = min(v_lo + blk * 32 + j * RPI + lane / CHUNKS, v_max);
+            __builtin_amdgcn_global_load_lds((const void *)(Wq + (int64_t)v * d + kb + wch[j]),
+                                             (lds_void_t *)(smem + wbase + slot * W_TILE + j * 1024), 16, 0,
+                                             kStream);
+        }
+#pragma unroll
+        for (int j = 0; j < LH; ++j)
+            __builtin_amdgcn_global_load_lds((const void *)(hsrc[j] + kb),
+                                             (lds_void_t *)(smem + H_BASE + slot * H_TILE + (j * 4 + wave) * 1024),
+                                             16, 0, 0);
+    };
+    // W scales of block blk (64 entries from its first row, clamped) into slot blk & 1
+    auto issue_wscale = [&](int blk) {
+        __builtin_amdgcn_global_load_lds((const void *)(ws + min(v_lo + blk * 32 + lane, v_max)),
+                                         (lds_void_t *)(smem + sbase + 256 + (blk & 1) * 256), 4, 0, 0);
+    };
+
+    const int fr = lane & 31, hi = lane >> 5;
+    const int lane_chunk = ((2 * hi) ^ swz(fr)) * 16;
+    const int a_addr = wbase + fr * ROW_BYTES + lane_chunk;
+    const int b_addr = H_BASE + fr * ROW_BYTES + lane_chunk;
+    auto frag = [&](int addr, int s) {
+        const i32x4_t lo = *(const i32x4_t *)(smem + (addr ^ (64 * s)));
+        const i32x4_t up = *(const i32x4_t *)(smem + (addr ^ (64 * s + 16)));
+        return i32x8_t{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+    };
+
+    f32x16_t acc[AM], held[NBK][AM];
+#pragma unroll
+    for (int bm = 0; bm < AM; ++bm)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            acc[bm][e] = 0.0f;
+
+    // the scales first (older than every tile, so the first wait covers them), then
+    // NSTAGE - 1 steps of the stream
+    __builtin_amdgcn_global_load_lds((const void *)(hs + min(lane, rows - 1)), (lds_void_t *)(smem + sbase), 4, 0,
+                                     0);
+    issue_wscale(0);
+    const int npre = min(NSTAGE - 1, ntiles);
+    for (int g = 0; g < npre; ++g)
+        issue(g, g);
+
+    const float *sch = (const float *)(smem + sbase);
+    int rs = 0;
+    for (int g = 0; g < ntiles; ++g) {
+        wait_tiles_upto_fp8<T, NSTAGE - 2>(min(NSTAGE - 2, ntiles - 1 - g));
+        bar();   // every wave's part of step g landed; every wave is done with step g-1
+        if (g + NSTAGE - 1 < ntiles)
+            issue(rs == 0 ? NSTAGE - 1 : rs - 1, g + NSTAGE - 1);
+        const int blk = g / nk, kt = g - blk * nk;
+        if (kt == 0 && blk + 1 < nblocks)
+            issue_wscale(blk + 1);   // slot (blk + 1) & 1 was last read at block blk - 1's end
+#pragma unroll
+        for (int s = 0; s < BK / 64; ++s) {
+            const i32x8_t af = frag(a_addr + rs * W_TILE, s);
+            i32x8_t bf[AM];
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm)
+                bf[bm] = frag(b_addr + rs * H_TILE + bm * 32 * ROW_BYTES, s);
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm)
+                acc[bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[bm], acc[bm], 0, 0, 0, 127, 0, 127);
+        }
+        rs = (rs + 1 == NSTAGE) ? 0 : rs + 1;
+        if (kt == nk - 1) {
+            // This block's W scales were requested at the first step of the previous block,
+            // after the refill of step (blk - 1) nk + NSTAGE - 1.  The step waits cover that
+            // request once a younger tile has been waited for, i.e. when
+            // (blk - 1) nk + NSTAGE <= blk nk + nk - 1; with fewer K tiles per block
+            // (d <= 384 here) wait for everything in flight instead.
+            if (2 * nk - 1 < NSTAGE)
+                wait_vm<0>();
+            // sum * (scale_h * scale_w); lane (fr, hi) holds, in accumulators 4 gq .. 4 gq + 3,
+            // vocabulary rows 8 gq + 4 hi + (0..3) of the block for masked row 32 bm + fr
+            const float *scw = (const float *)(smem + sbase + 256 + (blk & 1) * 256);
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm) {
+                const float h = sch[bm * 32 + fr];
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const f32x4_t w = *(const f32x4_t *)(scw + gq * 8 + hi * 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[bm][gq * 4 + e] = acc[bm][gq * 4 + e] * (h * w[e]);
+                }
+            }
+            lowm::lowm_block_done<AM, NBK, true>(held, acc, blk, nblocks, v_lo, v_hi, rows, fr, hi, out, ldo);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_rows_e4m3(const void *X, bool in_bf16, int64_t d, const int32_t *row_idx, int64_t rows,
@@ -432,6 +605,23 @@ hipError_t launch_quantize_rows_e4m3(const void *X, bool in_bf16, int64_t d, con
     else
         hipLaunchKernelGGL(quantize_rows_e4m3_kernel<false>, grid, dim3(256), 0, stream, X, (int32_t)d, row_idx,
                            rows, q, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8_lowm(const uint8_t *Hq, const float *hs, int64_t rows, const uint8_t *Wq, const float *ws,
+                                int64_t V, int64_t d, void *out, int64_t ldo, hipStream_t stream)
+{
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    // one workgroup (four streams) per CU, but never fewer than 32 rows per stream
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cus, (V + 127) / 128));
+    if (rows <= 32)
+        hipLaunchKernelGGL((gather_gemm_fp8_lowm_kernel<1, 7>), dim3(grid), dim3(256), 0, stream, Hq, hs,
+                           (int32_t)rows, Wq, ws, (int32_t)V, (int32_t)d, (__bf16 *)out, ldo);
+    else
+        hipLaunchKernelGGL((gather_gemm_fp8_lowm_kernel<2, 6>), dim3(grid), dim3(256), 0, stream, Hq, hs,
+                           (int32_t)rows, Wq, ws, (int32_t)V, (int32_t)d, (__bf16 *)out, ldo);
     return hipGetLastError();
 }
 

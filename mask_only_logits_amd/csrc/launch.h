@@ -76,4 +76,9 @@ hipError_t launch_quantize_rows_e4m3(const void *X, bool in_bf16, int64_t d, con
 hipError_t launch_gemm_fp8(const uint8_t *Hq, const float *hs, int64_t rows, const uint8_t *Wq, const float *ws,
                            int64_t V, int64_t d, void *out, int64_t ldo, int group_m, int nwaves, hipStream_t stream);
 
+// The same logits for rows <= 64 (d % 128 == 0): a W-streaming kernel, bit-identical to
+// launch_gemm_fp8.
+hipError_t launch_gemm_fp8_lowm(const uint8_t *Hq, const float *hs, int64_t rows, const uint8_t *Wq, const float *ws,
+                                int64_t V, int64_t d, void *out, int64_t ldo, hipStream_t stream);
+
 }  // namespace mosaic

@@ -42,13 +42,15 @@ int64_t checked_bytes(int64_t rows, int64_t V, int64_t esize)
 }
 
 // Debug/tuning override read on every call:
-// MOSAIC_TUNE="variant=<n>,group_m=<g>,waves=<w>" (waves: the FP8 kernel's 4 or 8).
+// MOSAIC_TUNE="variant=<n>,group_m=<g>,waves=<w>,fp8lowm=0" (waves: the FP8 kernel's 4 or
+// 8; fp8lowm=0: FP8 chunks of at most 64 rows also take the tiled FP8 kernel).
 // A forced variant that cannot run the call's shape is ignored.  For the fused consumer,
 // variant=16 selects its 32 x 32 x 16 MFMA form (default: 16 x 16 x 32).
 struct Tune {
     int variant = -1;
     int group_m = 0;
     int waves = 8;   // FP8 kernel: two waves per SIMD, measured 1% faster than one
+    bool fp8_lowm = true;   // FP8 chunks of at most 64 rows take the W-streaming kernel
 };
 
 Tune read_tune()
@@ -64,6 +66,8 @@ Tune read_tune()
         t.group_m = atoi(p + 8);
     if ((p = strstr(e, "waves=")) && atoi(p + 6) == 4)
         t.waves = 4;
+    if ((p = strstr(e, "fp8lowm=")) && atoi(p + 8) == 0)
+        t.fp8_lowm = false;
     return t;
 }
 
@@ -454,10 +458,12 @@ mosaic_status_t mosaic_masked_logits_fp8(const void *H, int64_t L, int64_t d, co
         const int64_t r0 = k * C;
         const int64_t r1 = (r0 + C < M) ? r0 + C : M;
         void *chunk_out = (char *)out + r0 * V * 2;
+        const bool lowm = t.fp8_lowm && r1 - r0 <= 64;
         if (mosaic::launch_quantize_rows_e4m3(H, true, d, idx + r0, r1 - r0, hq, hs, (hipStream_t)stream) !=
                 hipSuccess ||
-            mosaic::launch_gemm_fp8(hq, hs, r1 - r0, Wq, w_scale, V, d, chunk_out, V, t.group_m, t.waves,
-                                    (hipStream_t)stream) != hipSuccess)
+            (lowm ? mosaic::launch_gemm_fp8_lowm(hq, hs, r1 - r0, Wq, w_scale, V, d, chunk_out, V, (hipStream_t)stream)
+                  : mosaic::launch_gemm_fp8(hq, hs, r1 - r0, Wq, w_scale, V, d, chunk_out, V, t.group_m, t.waves,
+                                            (hipStream_t)stream)) != hipSuccess)
             return MOSAIC_ERR_DEVICE;
     }
     return MOSAIC_OK;

@@ -122,3 +122,25 @@ def test_dream_shape_low_m_all_rows(m):
     out = m.mosaic_masked_logits_fp8(wl.H.to(DEV), torch.from_numpy(idx).to(DEV), Wq, ws)
     torch.cuda.synchronize()
     assert_close(out, oracle.masked_logits_fp8(wl.H, idx, wl.W), "fp8 lowm")
+
+
+LOWM_CASES = [
+    # (L, d, V, M): chunks of at most 64 rows take the W-streaming FP8 kernel
+    (300, 128, 1001, 20), (300, 256, 3, 1), (300, 384, 4097, 33), (300, 3584, 5000, 64),
+    # several blocks per wave: padding blocks (1024 waves own 128 or 129 rows), two store bursts
+    (300, 256, 131584, 40), (300, 128, 300000, 20),
+]
+
+
+@pytest.mark.parametrize("L,d,V,M", LOWM_CASES)
+def test_lowm_kernel_parity_and_bit_identity(m, monkeypatch, L, d, V, M):
+    wl = inputs.make_random(L + 7 * d + V + M, L=L, d=d, V=V, M=M, dtype="bf16")
+    idx = oracle.mask_compact(wl.tokens, wl.mask_id)
+    H, idx_d = wl.H.to(DEV), torch.from_numpy(idx).to(DEV)
+    Wq, ws = m.mosaic_quantize_rows_fp8(wl.W.to(DEV))
+    out = m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws)
+    monkeypatch.setenv("MOSAIC_TUNE", "fp8lowm=0")          # the tiled FP8 kernel
+    tiled = m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, tiled)
+    assert_close(out, oracle.masked_logits_fp8(wl.H, idx, wl.W), f"fp8 lowm {d},{V},{M}")
