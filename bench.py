@@ -17,6 +17,12 @@ go to stderr.
                time measured by HIP events on the stream the kernels run on
   cpu_baseline the CPU oracle (fp64, OpenMP) timed on a bounded sample of rows
 
+Warm-up (untimed): by default at least WARMUP_MIN_STEPS steps and at least
+WARMUP_MIN_SECONDS of work.  The clock of a chip that was idle takes some tens of
+milliseconds to settle under this load (the first launches of a run are up to 25%
+off the steady rate), so a fixed count of 1-ms steps would time that transient
+instead of the steady state.  --warmup N runs exactly N steps instead.
+
 --path selects what the step does after compaction (default: logits):
   logits        the bf16 logits of every masked row, stored ([M, V])
   argmax_lse    each masked row reduced in the kernel to (max, first argmax,
@@ -42,6 +48,8 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 LOWM_VARIANTS = (6, 20)        # the W-streaming low-M kernels: HBM-bound
+WARMUP_MIN_STEPS = 3
+WARMUP_MIN_SECONDS = 0.15
 
 
 def log(*a):
@@ -91,6 +99,28 @@ def measured_traffic(workload: str, path: str = "logits", prof_dir: str | None =
     if t.get("kernel_source_hash") != kernel_source_hash(path):
         return None
     return t.get("bytes_per_launch")
+
+
+def warm_up(step, n_fixed=None, min_steps=WARMUP_MIN_STEPS, min_seconds=WARMUP_MIN_SECONDS, sync=None,
+            clock=time.perf_counter) -> int:
+    """Run untimed steps; return how many ran.
+
+    n_fixed: exactly that many.  Otherwise at least min_steps, and more until
+    min_seconds of wall time have passed with the device synchronized after each step
+    (so wall time is device time)."""
+    if n_fixed is not None:
+        for _ in range(n_fixed):
+            step()
+        if sync:
+            sync()
+        return n_fixed
+    n, t0 = 0, clock()
+    while n < min_steps or clock() - t0 < min_seconds:
+        step()
+        if sync:
+            sync()
+        n += 1
+    return n
 
 
 def host_info():
@@ -232,7 +262,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: at least %d steps and %.2f s of work)"
+                         % (WARMUP_MIN_STEPS, WARMUP_MIN_SECONDS))
     ap.add_argument("--workload", default="long_logits")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -368,8 +400,8 @@ def main():
             ev[i][2].record(stream)
         return m
 
-    for _ in range(args.warmup):
-        step()
+    n_warmup = warm_up(step, args.warmup, sync=torch.cuda.synchronize)
+    log(f"[bench] warm-up: {n_warmup} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -423,7 +455,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": n_warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

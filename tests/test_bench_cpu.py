@@ -7,6 +7,8 @@
   KiB fetched (128-byte requests counted as 64 bytes) and B KiB written, the scales are
   2 and 1, and the GEMM's mean per dispatch is scaled the same way;
 - measured_traffic returns the figure only while its source hash is the current one;
+- the default warm-up runs at least the minimum count of steps and keeps going until
+  the minimum time has passed; an explicit count runs exactly that many;
 - bench.py measures one GPU: --gpus 2 exits with status 2 and says so.
 """
 import csv
@@ -84,6 +86,34 @@ def test_no_traffic_without_both_counters(tmp_path):
     bench.summarize_profile(str(raw), "wl", 4, "logits", prof_dir=str(prof))
     assert not (prof / "traffic_gather_gemm_wl.json").exists()
     assert (prof / "gather_gemm_wl_rocprof.md").exists()
+
+
+class _FakeClock:
+    """Wall clock that advances by a fixed time per step."""
+
+    def __init__(self, step_s):
+        self.t, self.step_s = 0.0, step_s
+
+    def __call__(self):
+        return self.t
+
+    def step(self):
+        self.t += self.step_s
+
+
+def test_warm_up_by_time_and_by_count():
+    # 1-ms steps: 0.15 s of work needs 150 steps
+    clk = _FakeClock(0.001)
+    syncs = []
+    n = bench.warm_up(clk.step, None, min_steps=3, min_seconds=0.15, sync=lambda: syncs.append(1), clock=clk)
+    assert n == 150 and len(syncs) == 150
+    # 100-ms steps: the minimum count decides
+    clk = _FakeClock(0.1)
+    assert bench.warm_up(clk.step, None, min_steps=3, min_seconds=0.15, clock=clk) == 3
+    # an explicit count runs exactly that many, including none
+    clk = _FakeClock(0.001)
+    assert bench.warm_up(clk.step, 5, clock=clk) == 5 and abs(clk.t - 0.005) < 1e-12
+    assert bench.warm_up(clk.step, 0, clock=clk) == 0
 
 
 def test_more_than_one_gpu_is_refused():
