@@ -275,6 +275,10 @@ def main():
                     help="after the timed steps, time as many again with a cache-evicting pass over a buffer of "
                          "this many MiB before each (reported under detail.flushed); default: 512 for the "
                          "HBM-bound low-M kernel, else off")
+    ap.add_argument("--compare-vendor", action="store_true",
+                    help="after the timed steps, time the vendor GEMM (torch.mm, i.e. hipBLASLt) on the same "
+                         "chunks of the masked rows, gathered into a dense matrix beforehand (reported under "
+                         "detail.vendor_gemm; bf16 logits path only)")
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="summarize rocprofv3 CSV output found under DIR into profiles/ and exit")
     ap.add_argument("--path", choices=("logits", "argmax_lse", "dense_select", "fp8"), default="logits",
@@ -498,6 +502,41 @@ def main():
         else:
             result["detail"]["flushed"]["achieved_tflops"] = round(flop / (fmed / 1e3) / 1e12, 2)
         log(f"[bench] with a {flush_mib} MiB cache flush before each step: GEMM median {fmed:.3f} ms")
+
+    if args.compare_vendor:
+        if wl.dtype != "bf16" or args.path != "logits":
+            log("[bench] --compare-vendor times the bf16 logits path only")
+        else:
+            # The vendor's dense GEMM on the same chunks.  The masked rows are gathered into a
+            # dense matrix beforehand, outside the timing, so it does neither the gather nor
+            # the compaction: a reference for the GEMM, not an implementation of the path.
+            Hg = H[idx[:M].long()].contiguous()
+            Wt = W.t()
+            rows_c = M if launches == 1 else C
+            vout = torch.empty((rows_c, V), dtype=torch.bfloat16, device=dev)
+
+            def vstep():
+                for r0 in range(0, M, rows_c):
+                    r1 = min(M, r0 + rows_c)
+                    torch.mm(Hg[r0:r1], Wt, out=vout[: r1 - r0])
+
+            warm_up(vstep, args.warmup, sync=torch.cuda.synchronize)
+            va, vb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            va.record()
+            for _ in range(args.steps):
+                vstep()
+            vb.record()
+            torch.cuda.synchronize()
+            vms = va.elapsed_time(vb) / args.steps
+            vtf = flop / (vms / 1e3) / 1e12
+            result["detail"]["vendor_gemm"] = {
+                "kernel": "torch.mm (hipBLASLt) on the masked rows gathered beforehand, same chunks",
+                "ms_per_step": round(vms, 4), "tflops": round(vtf, 1),
+                "gemm_over_vendor": round(achieved / vtf, 4)}
+            log(f"[bench] vendor GEMM on pre-gathered rows: {vms:.3f} ms/step = {vtf:.1f} TFLOP/s "
+                f"(this GEMM {achieved / vtf:.3f} of it)")
+            del Hg, vout
 
     if args.profile_copy_mib:
         n = args.profile_copy_mib * (1 << 20) // 4
