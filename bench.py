@@ -340,7 +340,7 @@ def main():
             sys.exit(2)
         out = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
         Wq, wsc = mosaic.mosaic_quantize_rows_fp8(W)          # the weights, quantized once
-        ws8 = torch.empty(mosaic.mosaic_logits_fp8_workspace_bytes(rows_per_launch, d), dtype=torch.uint8,
+        ws8 = torch.empty(max(16, mosaic.mosaic_logits_fp8_workspace_bytes(M, C, d)), dtype=torch.uint8,
                           device=dev)
         variant = None
         log(f"[bench] M={M} chunk_rows={C} launches={launches} path=fp8 (E4M3 per-row scales) "
@@ -362,7 +362,7 @@ def main():
         rmax = torch.empty(M, dtype=torch.float32, device=dev)
         rarg = torch.empty(M, dtype=torch.int32, device=dev)
         rlse = torch.empty(M, dtype=torch.float32, device=dev)
-        ws = torch.empty(max(16, mosaic.mosaic_logits_argmax_lse_workspace_bytes(rows_per_launch, V)),
+        ws = torch.empty(max(16, mosaic.mosaic_logits_argmax_lse_workspace_bytes(M, C, V)),
                          dtype=torch.uint8, device=dev)
         variant = None
         log(f"[bench] M={M} chunk_rows={C} launches={launches} path=argmax_lse (no logits stored) "

@@ -29,8 +29,9 @@
  *
  * Conventions shared by every entry point
  *   - Every array pointer is a DEVICE pointer owned by the caller.  The library never
- *     allocates, frees or synchronises; all work is enqueued on `stream` (a
- *     hipStream_t passed as void*, NULL = the null stream) and is asynchronous.
+ *     allocates, frees or synchronises (the MOSAIC_CHECK_IDX=1 debug mode below
+ *     excepted); all work is enqueued on `stream` (a hipStream_t passed as void*,
+ *     NULL = the null stream) and is asynchronous.
  *   - Every function returns a status and prints nothing.  All argument validation
  *     happens before anything is enqueued; on INVALID_ARG or UNSUPPORTED no output
  *     is touched.  MOSAIC_ERR_DEVICE means a launch failed (earlier chunks of a
@@ -65,22 +66,35 @@ const char *mosaic_status_string(mosaic_status_t s);
 
 /* ---------------------------------------------------------------- compaction --- */
 
+/* Workspace bytes the three compaction calls need for L positions ([MR] 核心组件 1
+ * and [MP] §2.2 take the mask indices as the kernel's input; building them needs no
+ * intermediate buffer in this design).  Always 0: each workgroup counts the masked
+ * positions before its own segment itself, so no cross-workgroup state exists.  The
+ * calls take a workspace anyway so that a caller written against this query keeps
+ * working if a later design needs one. */
+size_t mosaic_mask_compact_workspace_bytes(int64_t L);
+
 /* Step 1 for one sequence ([MR] 核心组件 1 takes "the mask indices" as an input; [MP]
  * §2.2 addresses rows through them).
- *   tokens  int32[L]  token ids; position p is masked when tokens[p] == mask_id.
- *   idx     int32[L]  capacity L; on return idx[0..M) = the masked positions in
- *                     ascending order (entries from M on are left untouched).
- *   count   int32[1]  on return M.
+ *   tokens     int32[L]  token ids; position p is masked when tokens[p] == mask_id.
+ *   idx        int32[L]  capacity L; on return idx[0..M) = the masked positions in
+ *                        ascending order (entries from M on are left untouched).
+ *   count      int32[1]  on return M.
+ *   workspace  device memory of at least mosaic_mask_compact_workspace_bytes(L) bytes
+ *              (0 today: NULL with workspace_bytes 0 is the usual call); owned by the
+ *              caller, untouched.
  * L == 0 writes count = 0.  L >= 2^31 -> UNSUPPORTED.  Null tokens/idx with L > 0,
- * null count, or L < 0 -> INVALID_ARG.  One launch of at most 64 workgroups; needs no
- * workspace. */
+ * null count, L < 0, workspace_bytes below the query's value, or a NULL workspace
+ * with workspace_bytes > 0 -> INVALID_ARG.  One launch of at most 64 workgroups. */
 mosaic_status_t mosaic_mask_compact(const int32_t *tokens, int64_t L, int32_t mask_id,
-                                    int32_t *idx, int32_t *count, void *stream);
+                                    int32_t *idx, int32_t *count,
+                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /* Same as mosaic_mask_compact with a flag array: position p is masked when
  * flags[p] != 0.  flags is uint8[L]. */
 mosaic_status_t mosaic_mask_compact_flags(const uint8_t *flags, int64_t L,
-                                          int32_t *idx, int32_t *count, void *stream);
+                                          int32_t *idx, int32_t *count,
+                                          void *workspace, size_t workspace_bytes, void *stream);
 
 /* Step 1 for a ragged batch of nseq sequences concatenated into tokens[L].
  *   seq_offsets  int32[nseq+1]  sequence s owns positions [seq_offsets[s], seq_offsets[s+1]);
@@ -90,11 +104,12 @@ mosaic_status_t mosaic_mask_compact_flags(const uint8_t *flags, int64_t L,
  *                               sequence, ascending within each (so ascending overall).
  *   idx_offsets  int32[nseq+1]  on return CSR offsets: sequence s's masked rows are
  *                               idx[idx_offsets[s] .. idx_offsets[s+1]); idx_offsets[nseq] = M.
+ *   workspace    as for mosaic_mask_compact.
  * nseq <= 0 -> INVALID_ARG.  Two launches (compaction, then the CSR offsets). */
 mosaic_status_t mosaic_mask_compact_batched(const int32_t *tokens, int64_t L,
                                             const int32_t *seq_offsets, int32_t nseq,
                                             int32_t mask_id, int32_t *idx, int32_t *idx_offsets,
-                                            void *stream);
+                                            void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------- logits --- */
 
@@ -109,9 +124,14 @@ mosaic_status_t mosaic_mask_compact_batched(const int32_t *tokens, int64_t L,
  *                                       every logits entry point first checks idx on the
  *                                       device, waits for the answer (synchronous) and
  *                                       returns INVALID_ARG, enqueuing no compute and
- *                                       touching no output, if a value is out of range
- *                                       (a debug mode; it allocates a 4-byte flag once
- *                                       per device).
+ *                                       touching no output, if a value is out of range.
+ *                                       This debug mode breaks two conventions above on
+ *                                       purpose: it allocates a 4-byte flag once per
+ *                                       (device, stream) pair, kept until the process
+ *                                       ends, and it synchronises the stream.  Checked
+ *                                       calls on different streams use different flags;
+ *                                       checked calls that overlap on one stream from
+ *                                       several host threads are not supported.
  *   W      [V, d] row-major, in_dtype   LM-head weight (K-contiguous rows).
  *   out    [M, V] row-major, out_dtype  row i holds the logits of position idx[i].
  *   chunk_rows  max_num_logits: <= 0 or >= M runs one chunk; otherwise
@@ -155,9 +175,9 @@ mosaic_status_t mosaic_masked_logits(const void *H, int64_t L, int64_t d,
  *              receives the same bits mosaic_masked_logits would write.
  *   row_max    float[M], row_argmax int32[M], row_lse float[M]: device, 4-byte aligned.
  *   workspace  device scratch of at least
- *              mosaic_logits_argmax_lse_workspace_bytes(C, V) bytes, C = the rows of
- *              the largest chunk (M when unchunked), 16-byte aligned; owned by the
- *              caller; its contents on entry do not matter and on return are undefined.
+ *              mosaic_logits_argmax_lse_workspace_bytes(M, chunk_rows, V) bytes,
+ *              16-byte aligned; owned by the caller; its contents on entry do not
+ *              matter and on return are undefined.
  * Results are deterministic and do not depend on chunk_rows.  M == 0: MOSAIC_OK and
  * nothing is enqueued.  V == 0 with M > 0, a NULL required pointer, misalignment or a
  * short workspace: INVALID_ARG; nothing is enqueued and no output is touched. */
@@ -170,10 +190,11 @@ mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_
                                                 void *workspace, int64_t workspace_bytes,
                                                 void *stream);
 
-/* Workspace bytes for launches of `rows` rows over V vocabulary entries:
- * 12 * ceil(V / 256) * rows (three 4-byte partials per row and 256-entry tile), or -1
- * on a negative size or int64 overflow. */
-int64_t mosaic_logits_argmax_lse_workspace_bytes(int64_t rows, int64_t V);
+/* Workspace bytes of mosaic_masked_logits_argmax_lse for M rows in chunks of
+ * chunk_rows over V vocabulary entries: 12 * ceil(V / 256) * C, with C the rows of the
+ * largest chunk (three 4-byte partials per row and 256-entry tile; one chunk's partials
+ * are live at a time), 0 for M == 0, or -1 on a negative size or int64 overflow. */
+int64_t mosaic_logits_argmax_lse_workspace_bytes(int64_t M, int64_t chunk_rows, int64_t V);
 
 /* ---------------------------------------------------------- FP8 LM head --- */
 
@@ -192,9 +213,10 @@ mosaic_status_t mosaic_quantize_rows_fp8(const void *X, int64_t nsrc, int64_t d,
                                          const int32_t *row_idx, int64_t rows, uint8_t *q, float *scale,
                                          void *stream);
 
-/* Workspace bytes of mosaic_masked_logits_fp8 for chunks of `rows` rows:
- * rows * d rounded up to 16, plus 4 * rows; -1 on a negative size or overflow. */
-int64_t mosaic_logits_fp8_workspace_bytes(int64_t rows, int64_t d);
+/* Workspace bytes of mosaic_masked_logits_fp8 for M rows in chunks of chunk_rows:
+ * C * d rounded up to 16, plus 4 * C, with C the rows of the largest chunk; 0 for
+ * M == 0; -1 on a negative size or overflow. */
+int64_t mosaic_logits_fp8_workspace_bytes(int64_t M, int64_t chunk_rows, int64_t d);
 
 /* out[i, v] = (sum_k q_h[i][k] * Wq[v][k]) * scale_h[i] * w_scale[v], rounded to bf16, for
  * i < M, v < V, where q_h[i], scale_h[i] quantize row H[idx[i]] as above.  Each chunk
@@ -205,8 +227,8 @@ int64_t mosaic_logits_fp8_workspace_bytes(int64_t rows, int64_t d);
  *            mosaic_quantize_rows_fp8 on W.
  *   out      [M, V] bf16 (out_dtype must be BF16), 16-byte aligned.
  *   chunk_rows, stream: as for mosaic_masked_logits.
- *   workspace >= mosaic_logits_fp8_workspace_bytes(C, d) bytes, C = the rows of the
- *            largest chunk; 16-byte aligned; contents undefined on return.
+ *   workspace >= mosaic_logits_fp8_workspace_bytes(M, chunk_rows, d) bytes; 16-byte
+ *            aligned; contents undefined on return.
  * d % 128 == 0 (else UNSUPPORTED).  M == 0 or V == 0: OK, nothing enqueued.  Results
  * do not depend on chunk_rows. */
 mosaic_status_t mosaic_masked_logits_fp8(const void *H, int64_t L, int64_t d, const int32_t *idx, int64_t M,
@@ -241,6 +263,14 @@ mosaic_status_t mosaic_logits_bytes(int64_t rows, int64_t V, mosaic_dtype_t dt, 
  * unsupported. */
 int mosaic_logits_variant(int64_t M, int64_t V, int64_t d, mosaic_dtype_t in_dtype,
                           mosaic_dtype_t out_dtype);
+
+/* ---------------------------------------------------------------- debugging --- */
+
+/* The library reads two debug variables from the environment once per process, at the
+ * first call that needs them: MOSAIC_CHECK_IDX (see mosaic_masked_logits) and
+ * MOSAIC_TUNE (forces a kernel variant or tile grouping, for tests and sweeps).  This
+ * call reads them again; calls already running keep the values they started with. */
+void mosaic_debug_reload_env(void);
 
 #ifdef __cplusplus
 }

@@ -1408,8 +1408,8 @@ gather_gemm_lowm_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict_
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     char *smem = smem_all + wave * WAVE_LDS;
     const int64_t nw = (int64_t)gridDim.x * 4, gw = (int64_t)blockIdx.x * 4 + wave;
-    const int v_lo = (int)((gw * V) / nw);
-    const int v_hi = (int)(((gw + 1) * V) / nw);
+    const int v_lo = lowm::range_bound(gw, nw, V);
+    const int v_hi = lowm::range_bound(gw + 1, nw, V);
     const int nblocks = (v_hi - v_lo + 31) / 32;
     const int nk = d / BK;
     const int ntiles = nblocks * nk;              // flattened (block, k tile) stream
@@ -1554,11 +1554,11 @@ gather_gemm_lowm_shared_kernel(const __bf16 *__restrict__ H, const int32_t *__re
     const int64_t wg = gridDim.x % 8 == 0 ? (int64_t)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8
                                           : (int64_t)blockIdx.x;
     const int64_t nw = (int64_t)gridDim.x * 4, gw = wg * 4 + wave;
-    const int v_lo = (int)((gw * V) / nw);
-    const int v_hi = (int)(((gw + 1) * V) / nw);
+    const int v_lo = lowm::range_bound(gw, nw, V);
+    const int v_hi = lowm::range_bound(gw + 1, nw, V);
     const int v_max = max(v_hi - 1, 0);           // clamp for padding rows (V >= 1)
-    // every range is at most ceil(V / nw) rows: the same block count for all waves
-    const int nblocks = (int)(((V + nw - 1) / nw + 31) / 32);
+    // the same block count for all waves (that of the longest range)
+    const int nblocks = lowm::range_blocks(nw, V);
     const int nk = d / BK;
     const int ntiles = nblocks * nk;
 

@@ -476,10 +476,10 @@ gather_gemm_fp8_lowm_kernel(const uint8_t *__restrict__ Hq, const float *__restr
     const int64_t wg = gridDim.x % 8 == 0 ? (int64_t)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8
                                           : (int64_t)blockIdx.x;
     const int64_t nw = (int64_t)gridDim.x * 4, gw = wg * 4 + wave;
-    const int v_lo = (int)((gw * V) / nw);
-    const int v_hi = (int)(((gw + 1) * V) / nw);
+    const int v_lo = lowm::range_bound(gw, nw, V);
+    const int v_hi = lowm::range_bound(gw + 1, nw, V);
     const int v_max = max(v_hi - 1, 0);              // clamp for padding rows (V >= 1)
-    const int nblocks = (int)(((V + nw - 1) / nw + 31) / 32);
+    const int nblocks = lowm::range_blocks(nw, V);
     const int nk = d / BK;
     const int ntiles = nblocks * nk;
     auto swz = [](int r) { return (r >> 1) & 7; };

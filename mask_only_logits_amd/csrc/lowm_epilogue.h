@@ -17,6 +17,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+// Vocabulary range of wave g of nw (g = nw gives the end, V): [bound(g), bound(g + 1)).
+// Boundaries are g * V / nw rounded down to a multiple of 8 rows, so each lane's
+// 4-entry store run starts 4-aligned and takes the vector store path.
+__device__ __forceinline__ int range_bound(int64_t g, int64_t nw, int V)
+{
+    return g >= nw ? V : (int)(((g * V) / nw) & ~(int64_t)7);
+}
+
+// 32-row blocks of the longest range (at most ceil(V / nw) + 7 rows): every wave runs
+// this many, padding blocks included.
+__device__ __forceinline__ int range_blocks(int64_t nw, int V)
+{
+    return (int)(((V + nw - 1) / nw + 7 + 31) / 32);
+}
+
 // Low-M epilogue: store one finished 32-vocabulary-row block (AM x 32 masked rows) whose
 // first vocabulary row is vb; rows >= `rows` and vocabulary rows >= v_hi are not stored.
 // Lane (fr, hi) holds, in accumulators 4 gq .. 4 gq + 3 of block bm, vocabulary rows
@@ -35,7 +50,8 @@ __device__ __forceinline__ void lowm_store_block(const f32x16_t (&res)[AM], int 
             const int v = vb + gq * 8 + hi * 4;
             const float x0 = res[bm][gq * 4 + 0], x1 = res[bm][gq * 4 + 1];
             const float x2 = res[bm][gq * 4 + 2], x3 = res[bm][gq * 4 + 3];
-            const bool full = v + 3 < v_hi && (ldo & 3) == 0;
+            // a vector store needs its address aligned to its size (8 or 16 bytes)
+            const bool full = v + 3 < v_hi && (ldo & 3) == 0 && (v & 3) == 0;
             if constexpr (OUT_BF16) {
                 __bf16 *o = (__bf16 *)out + (int64_t)row * ldo + v;
                 if (full) {

@@ -16,6 +16,7 @@
 
 #include <map>
 #include <mutex>
+#include <utility>
 
 #include "../../include/mosaic.h"
 #include "launch.h"
@@ -41,7 +42,8 @@ int64_t checked_bytes(int64_t rows, int64_t V, int64_t esize)
     return n * esize;
 }
 
-// Debug/tuning override read on every call:
+// Debug/tuning override, read from the environment once per process (the first call
+// that needs it) and again on mosaic_debug_reload_env():
 // MOSAIC_TUNE="variant=<n>,group_m=<g>,waves=<w>,fp8lowm=0" (waves: the FP8 kernel's 4 or
 // 8; fp8lowm=0: FP8 chunks of at most 64 rows also take the tiled FP8 kernel).
 // A forced variant that cannot run the call's shape is ignored.  For the fused consumer,
@@ -51,11 +53,14 @@ struct Tune {
     int group_m = 0;
     int waves = 8;   // FP8 kernel: two waves per SIMD, measured 1% faster than one
     bool fp8_lowm = true;   // FP8 chunks of at most 64 rows take the W-streaming kernel
+    bool check_idx = false;   // MOSAIC_CHECK_IDX=1
 };
 
-Tune read_tune()
+Tune parse_env()
 {
     Tune t;
+    const char *c = getenv("MOSAIC_CHECK_IDX");
+    t.check_idx = c && c[0] == '1';
     const char *e = getenv("MOSAIC_TUNE");
     if (!e)
         return t;
@@ -71,28 +76,44 @@ Tune read_tune()
     return t;
 }
 
-// Debug mode MOSAIC_CHECK_IDX=1: before any compute is enqueued, check on the device
-// that every idx[i] (i < M) lies in [0, L), and wait for the answer.  A 4-byte device
-// flag is allocated once per device on first use.  Returns MOSAIC_OK (mode off, or all
-// indices valid), MOSAIC_ERR_INVALID_ARG (an index out of range) or MOSAIC_ERR_DEVICE.
+std::mutex g_env_mu;
+Tune g_env;
+bool g_env_read = false;
+
+Tune read_tune()
+{
+    std::lock_guard<std::mutex> lk(g_env_mu);
+    if (!g_env_read) {
+        g_env = parse_env();
+        g_env_read = true;
+    }
+    return g_env;
+}
+
+// Debug mode MOSAIC_CHECK_IDX=1 (read with MOSAIC_TUNE): before any compute is
+// enqueued, check on the device that every idx[i] (i < M) lies in [0, L), and wait for
+// the answer.  A 4-byte device flag is allocated on first use for each (device, stream)
+// pair, so checked calls on different streams never share a flag.  Returns MOSAIC_OK
+// (mode off, or all indices valid), MOSAIC_ERR_INVALID_ARG (an index out of range) or
+// MOSAIC_ERR_DEVICE.
 mosaic_status_t check_idx_if_asked(const int32_t *idx, int64_t M, int64_t L, hipStream_t stream)
 {
-    const char *e = getenv("MOSAIC_CHECK_IDX");
-    if (!e || e[0] != '1')
+    if (!read_tune().check_idx)
         return MOSAIC_OK;
     static std::mutex mu;
-    static std::map<int, int32_t *> flags;
+    static std::map<std::pair<int, hipStream_t>, int32_t *> flags;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return MOSAIC_ERR_DEVICE;
     int32_t *flag = nullptr;
     {
         std::lock_guard<std::mutex> lk(mu);
-        auto it = flags.find(dev);
+        const auto key = std::make_pair(dev, stream);
+        auto it = flags.find(key);
         if (it == flags.end()) {
             if (hipMalloc((void **)&flag, sizeof(int32_t)) != hipSuccess)
                 return MOSAIC_ERR_DEVICE;
-            flags[dev] = flag;
+            flags[key] = flag;
         } else {
             flag = it->second;
         }
@@ -163,6 +184,13 @@ int pick_variant(int64_t M, int64_t V, int64_t d, mosaic_dtype_t in, mosaic_dtyp
 
 extern "C" {
 
+void mosaic_debug_reload_env(void)
+{
+    std::lock_guard<std::mutex> lk(g_env_mu);
+    g_env = parse_env();
+    g_env_read = true;
+}
+
 const char *mosaic_status_string(mosaic_status_t s)
 {
     switch (s) {
@@ -200,10 +228,23 @@ int mosaic_logits_variant(int64_t M, int64_t V, int64_t d, mosaic_dtype_t in_dty
     return pick_variant(M, V, d, in_dtype, out_dtype);
 }
 
-mosaic_status_t mosaic_mask_compact(const int32_t *tokens, int64_t L, int32_t mask_id, int32_t *idx,
-                                    int32_t *count, void *stream)
+size_t mosaic_mask_compact_workspace_bytes(int64_t L)
 {
-    if (L < 0 || !count || (L > 0 && (!tokens || !idx)))
+    (void)L;   // each workgroup recounts the prefix before its segment: no shared state
+    return 0;
+}
+
+// The workspace arguments of the compaction calls: enough bytes for the query, and a
+// pointer wherever bytes are claimed.
+static bool compact_workspace_ok(int64_t L, const void *workspace, size_t workspace_bytes)
+{
+    return workspace_bytes >= mosaic_mask_compact_workspace_bytes(L) && (workspace || workspace_bytes == 0);
+}
+
+mosaic_status_t mosaic_mask_compact(const int32_t *tokens, int64_t L, int32_t mask_id, int32_t *idx,
+                                    int32_t *count, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (L < 0 || !count || (L > 0 && (!tokens || !idx)) || !compact_workspace_ok(L, workspace, workspace_bytes))
         return MOSAIC_ERR_INVALID_ARG;
     if (L > kMaxPos)
         return MOSAIC_ERR_UNSUPPORTED;
@@ -213,9 +254,9 @@ mosaic_status_t mosaic_mask_compact(const int32_t *tokens, int64_t L, int32_t ma
 }
 
 mosaic_status_t mosaic_mask_compact_flags(const uint8_t *flags, int64_t L, int32_t *idx, int32_t *count,
-                                          void *stream)
+                                          void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (L < 0 || !count || (L > 0 && (!flags || !idx)))
+    if (L < 0 || !count || (L > 0 && (!flags || !idx)) || !compact_workspace_ok(L, workspace, workspace_bytes))
         return MOSAIC_ERR_INVALID_ARG;
     if (L > kMaxPos)
         return MOSAIC_ERR_UNSUPPORTED;
@@ -226,9 +267,11 @@ mosaic_status_t mosaic_mask_compact_flags(const uint8_t *flags, int64_t L, int32
 
 mosaic_status_t mosaic_mask_compact_batched(const int32_t *tokens, int64_t L, const int32_t *seq_offsets,
                                             int32_t nseq, int32_t mask_id, int32_t *idx,
-                                            int32_t *idx_offsets, void *stream)
+                                            int32_t *idx_offsets, void *workspace, size_t workspace_bytes,
+                                            void *stream)
 {
-    if (L < 0 || nseq <= 0 || !seq_offsets || !idx_offsets || (L > 0 && (!tokens || !idx)))
+    if (L < 0 || nseq <= 0 || !seq_offsets || !idx_offsets || (L > 0 && (!tokens || !idx)) ||
+        !compact_workspace_ok(L, workspace, workspace_bytes))
         return MOSAIC_ERR_INVALID_ARG;
     if (L > kMaxPos)
         return MOSAIC_ERR_UNSUPPORTED;
@@ -318,13 +361,27 @@ mosaic_status_t mosaic_lazy_chunk_rows(int64_t M, int64_t V, mosaic_dtype_t out_
     return MOSAIC_OK;
 }
 
-int64_t mosaic_logits_argmax_lse_workspace_bytes(int64_t rows, int64_t V)
+// Rows of the largest chunk of a call over M rows ([DS] §3.2.2): M when unchunked.
+static int64_t largest_chunk_rows(int64_t M, int64_t chunk_rows)
+{
+    return mosaic_num_chunks(M, chunk_rows) <= 1 ? (M > 0 ? M : 0) : chunk_rows;
+}
+
+// The consumer's partials for launches of `rows` rows: 12 * ceil(V / 256) * rows bytes.
+static int64_t argmax_lse_partials_bytes(int64_t rows, int64_t V)
 {
     if (rows < 0 || V < 0)
         return -1;
     const int64_t ncol = (V + 255) / 256;
     const int64_t n = checked_bytes(ncol, rows, 12);
     return n < 0 ? -1 : n;
+}
+
+int64_t mosaic_logits_argmax_lse_workspace_bytes(int64_t M, int64_t chunk_rows, int64_t V)
+{
+    if (M < 0 || V < 0)
+        return -1;
+    return argmax_lse_partials_bytes(largest_chunk_rows(M, chunk_rows), V);
 }
 
 mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_t d, const int32_t *idx, int64_t M,
@@ -359,7 +416,7 @@ mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_
     const int64_t C = (K == 1) ? M : chunk_rows;
     if (C > kMaxPos || !mosaic::gather_gemm_grid_fits(mosaic::kVariantBf16DeferS4I8, C, V))
         return MOSAIC_ERR_UNSUPPORTED;
-    const int64_t need = mosaic_logits_argmax_lse_workspace_bytes(C, V);
+    const int64_t need = argmax_lse_partials_bytes(C, V);
     if (need < 0 || workspace_bytes < need)
         return MOSAIC_ERR_INVALID_ARG;
     // workspace: pmax, parg, psum, each [ceil(V/256)][C] 4-byte words
@@ -409,7 +466,9 @@ mosaic_status_t mosaic_quantize_rows_fp8(const void *X, int64_t nsrc, int64_t d,
                : MOSAIC_ERR_DEVICE;
 }
 
-int64_t mosaic_logits_fp8_workspace_bytes(int64_t rows, int64_t d)
+// The FP8 path's per-chunk buffer for launches of `rows` rows: codes [rows, d] (padded to
+// 16 bytes), then the row scales.
+static int64_t fp8_chunk_bytes(int64_t rows, int64_t d)
 {
     const int64_t codes = checked_bytes(rows, d, 1);
     if (codes < 0 || rows < 0)
@@ -418,6 +477,13 @@ int64_t mosaic_logits_fp8_workspace_bytes(int64_t rows, int64_t d)
     if (aligned > INT64_MAX - 4 * rows)
         return -1;
     return aligned + 4 * rows;
+}
+
+int64_t mosaic_logits_fp8_workspace_bytes(int64_t M, int64_t chunk_rows, int64_t d)
+{
+    if (M < 0 || d < 0)
+        return -1;
+    return fp8_chunk_bytes(largest_chunk_rows(M, chunk_rows), d);
 }
 
 mosaic_status_t mosaic_masked_logits_fp8(const void *H, int64_t L, int64_t d, const int32_t *idx, int64_t M,
@@ -444,7 +510,7 @@ mosaic_status_t mosaic_masked_logits_fp8(const void *H, int64_t L, int64_t d, co
     const int64_t C = (K == 1) ? M : chunk_rows;
     if (C > kMaxPos || ((C + 255) / 256) * ((V + 255) / 256) > 0x7fffffffLL)
         return MOSAIC_ERR_UNSUPPORTED;
-    const int64_t need = mosaic_logits_fp8_workspace_bytes(C, d);
+    const int64_t need = fp8_chunk_bytes(C, d);
     if (need < 0 || workspace_bytes < need)
         return MOSAIC_ERR_INVALID_ARG;
     // workspace: the chunk's codes [C, d], then its row scales [C]

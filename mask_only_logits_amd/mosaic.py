@@ -27,6 +27,7 @@ MOSAIC_BF16 = 1
 # Every symbol include/mosaic.h declares.
 EXPORTS = (
     "mosaic_status_string",
+    "mosaic_mask_compact_workspace_bytes",
     "mosaic_mask_compact",
     "mosaic_mask_compact_flags",
     "mosaic_mask_compact_batched",
@@ -40,6 +41,7 @@ EXPORTS = (
     "mosaic_quantize_rows_fp8",
     "mosaic_logits_fp8_workspace_bytes",
     "mosaic_masked_logits_fp8",
+    "mosaic_debug_reload_env",
 )
 
 
@@ -57,12 +59,15 @@ def _load() -> ctypes.CDLL:
     i64, i32, p, st = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int
     lib.mosaic_status_string.restype = ctypes.c_char_p
     lib.mosaic_status_string.argtypes = [st]
+    sz = ctypes.c_size_t
+    lib.mosaic_mask_compact_workspace_bytes.restype = sz
+    lib.mosaic_mask_compact_workspace_bytes.argtypes = [i64]
     lib.mosaic_mask_compact.restype = st
-    lib.mosaic_mask_compact.argtypes = [p, i64, i32, p, p, p]
+    lib.mosaic_mask_compact.argtypes = [p, i64, i32, p, p, p, sz, p]
     lib.mosaic_mask_compact_flags.restype = st
-    lib.mosaic_mask_compact_flags.argtypes = [p, i64, p, p, p]
+    lib.mosaic_mask_compact_flags.argtypes = [p, i64, p, p, p, sz, p]
     lib.mosaic_mask_compact_batched.restype = st
-    lib.mosaic_mask_compact_batched.argtypes = [p, i64, p, i32, i32, p, p, p]
+    lib.mosaic_mask_compact_batched.argtypes = [p, i64, p, i32, i32, p, p, p, sz, p]
     lib.mosaic_masked_logits.restype = st
     lib.mosaic_masked_logits.argtypes = [p, i64, i64, p, i64, p, i64, p, i64, st, st, p]
     lib.mosaic_num_chunks.restype = i64
@@ -74,13 +79,15 @@ def _load() -> ctypes.CDLL:
     lib.mosaic_masked_logits_argmax_lse.restype = st
     lib.mosaic_masked_logits_argmax_lse.argtypes = [p, i64, i64, p, i64, p, i64, p, i64, st, st, p, p, p, p, i64, p]
     lib.mosaic_logits_argmax_lse_workspace_bytes.restype = i64
-    lib.mosaic_logits_argmax_lse_workspace_bytes.argtypes = [i64, i64]
+    lib.mosaic_logits_argmax_lse_workspace_bytes.argtypes = [i64, i64, i64]
     lib.mosaic_quantize_rows_fp8.restype = st
     lib.mosaic_quantize_rows_fp8.argtypes = [p, i64, i64, st, p, i64, p, p, p]
     lib.mosaic_logits_fp8_workspace_bytes.restype = i64
-    lib.mosaic_logits_fp8_workspace_bytes.argtypes = [i64, i64]
+    lib.mosaic_logits_fp8_workspace_bytes.argtypes = [i64, i64, i64]
     lib.mosaic_masked_logits_fp8.restype = st
     lib.mosaic_masked_logits_fp8.argtypes = [p, i64, i64, p, i64, p, p, i64, p, i64, st, p, i64, p]
+    lib.mosaic_debug_reload_env.restype = None
+    lib.mosaic_debug_reload_env.argtypes = []
     lib.mosaic_lazy_chunk_rows.restype = st
     lib.mosaic_lazy_chunk_rows.argtypes = [i64, i64, st, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     return lib
@@ -126,6 +133,11 @@ def _check(status: int, where: str):
         raise MosaicError(status, where)
 
 
+def mosaic_debug_reload_env() -> None:
+    """Make the library read MOSAIC_TUNE and MOSAIC_CHECK_IDX from the environment again."""
+    lib.mosaic_debug_reload_env()
+
+
 def mosaic_status_string(status: int) -> str:
     return lib.mosaic_status_string(int(status)).decode()
 
@@ -154,8 +166,23 @@ def mosaic_lazy_chunk_rows(M: int, V: int, dtype: torch.dtype, budget_bytes: int
     return int(c.value), int(k.value)
 
 
+def mosaic_mask_compact_workspace_bytes(L: int) -> int:
+    """Workspace bytes the compaction calls need for L positions."""
+    return int(lib.mosaic_mask_compact_workspace_bytes(int(L)))
+
+
+def _compact_workspace(L: int, workspace: torch.Tensor | None, device):
+    """(pointer, bytes) of the compaction workspace, allocated if absent and needed."""
+    if workspace is None:
+        need = mosaic_mask_compact_workspace_bytes(L)
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return _dev(workspace, "workspace", torch.uint8), workspace.numel()
+
+
 def mosaic_mask_compact(tokens: torch.Tensor, mask_id: int, idx: torch.Tensor | None = None,
-                        count: torch.Tensor | None = None, stream=None):
+                        count: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
     """Masked positions of int32 `tokens` in ascending order -> (idx [L] int32, count [1] int32).
 
     Asynchronous: idx[:count] holds the list once the stream reaches this point."""
@@ -164,14 +191,16 @@ def mosaic_mask_compact(tokens: torch.Tensor, mask_id: int, idx: torch.Tensor | 
         idx = torch.empty(max(L, 1), dtype=torch.int32, device=tokens.device)
     if count is None:
         count = torch.empty(1, dtype=torch.int32, device=tokens.device)
+    ws, wsb = _compact_workspace(L, workspace, tokens.device)
     _check(lib.mosaic_mask_compact(_dev(tokens, "tokens", torch.int32), L, int(mask_id),
-                                   _dev(idx, "idx", torch.int32), _dev(count, "count", torch.int32),
+                                   _dev(idx, "idx", torch.int32), _dev(count, "count", torch.int32), ws, wsb,
                                    _stream(stream)), "mosaic_mask_compact")
     return idx, count
 
 
 def mosaic_mask_compact_flags(flags: torch.Tensor, idx: torch.Tensor | None = None,
-                              count: torch.Tensor | None = None, stream=None):
+                              count: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                              stream=None):
     """Positions with flags != 0 (uint8 or bool flags) -> (idx, count)."""
     if flags.dtype == torch.bool:
         flags = flags.view(torch.uint8)
@@ -180,15 +209,16 @@ def mosaic_mask_compact_flags(flags: torch.Tensor, idx: torch.Tensor | None = No
         idx = torch.empty(max(L, 1), dtype=torch.int32, device=flags.device)
     if count is None:
         count = torch.empty(1, dtype=torch.int32, device=flags.device)
+    ws, wsb = _compact_workspace(L, workspace, flags.device)
     _check(lib.mosaic_mask_compact_flags(_dev(flags, "flags", torch.uint8), L, _dev(idx, "idx", torch.int32),
-                                         _dev(count, "count", torch.int32), _stream(stream)),
+                                         _dev(count, "count", torch.int32), ws, wsb, _stream(stream)),
            "mosaic_mask_compact_flags")
     return idx, count
 
 
 def mosaic_mask_compact_batched(tokens: torch.Tensor, seq_offsets: torch.Tensor, mask_id: int,
                                 idx: torch.Tensor | None = None, idx_offsets: torch.Tensor | None = None,
-                                stream=None):
+                                workspace: torch.Tensor | None = None, stream=None):
     """Ragged batch -> (idx [L] global positions, idx_offsets [nseq+1] CSR)."""
     L = tokens.numel()
     nseq = seq_offsets.numel() - 1
@@ -196,10 +226,12 @@ def mosaic_mask_compact_batched(tokens: torch.Tensor, seq_offsets: torch.Tensor,
         idx = torch.empty(max(L, 1), dtype=torch.int32, device=tokens.device)
     if idx_offsets is None:
         idx_offsets = torch.empty(max(nseq + 1, 1), dtype=torch.int32, device=tokens.device)
+    ws, wsb = _compact_workspace(L, workspace, tokens.device)
     _check(lib.mosaic_mask_compact_batched(_dev(tokens, "tokens", torch.int32), L,
                                            _dev(seq_offsets, "seq_offsets", torch.int32), nseq, int(mask_id),
                                            _dev(idx, "idx", torch.int32),
-                                           _dev(idx_offsets, "idx_offsets", torch.int32), _stream(stream)),
+                                           _dev(idx_offsets, "idx_offsets", torch.int32), ws, wsb,
+                                           _stream(stream)),
            "mosaic_mask_compact_batched")
     return idx, idx_offsets
 
@@ -230,9 +262,9 @@ def mosaic_masked_logits(H: torch.Tensor, idx: torch.Tensor, W: torch.Tensor, M:
     return out
 
 
-def mosaic_logits_argmax_lse_workspace_bytes(rows: int, V: int) -> int:
-    """Workspace bytes mosaic_masked_logits_argmax_lse needs for launches of `rows` rows."""
-    n = int(lib.mosaic_logits_argmax_lse_workspace_bytes(int(rows), int(V)))
+def mosaic_logits_argmax_lse_workspace_bytes(M: int, chunk_rows: int, V: int) -> int:
+    """Workspace bytes mosaic_masked_logits_argmax_lse needs for M rows in chunks of chunk_rows."""
+    n = int(lib.mosaic_logits_argmax_lse_workspace_bytes(int(M), int(chunk_rows), int(V)))
     if n < 0:
         raise ValueError("workspace size overflows")
     return n
@@ -250,7 +282,7 @@ def mosaic_masked_logits_argmax_lse(H: torch.Tensor, idx: torch.Tensor, W: torch
     The logits are stored only if `store_logits` (or `out` is given): then `out`
     ([M, V] bf16, allocated if absent) holds them and is returned as the fourth item,
     else the fourth item is None.  `workspace` (uint8, allocated if absent) must hold
-    mosaic_logits_argmax_lse_workspace_bytes(min(M, chunk_rows or M), V) bytes."""
+    mosaic_logits_argmax_lse_workspace_bytes(M, chunk_rows, V) bytes."""
     if H.dim() != 2 or W.dim() != 2 or H.shape[1] != W.shape[1]:
         raise ValueError("H must be [L, d] and W [V, d]")
     L, d = H.shape
@@ -269,8 +301,7 @@ def mosaic_masked_logits_argmax_lse(H: torch.Tensor, idx: torch.Tensor, W: torch
     for name, t in (("row_max", row_max), ("row_argmax", row_argmax), ("row_lse", row_lse)):
         if t.numel() < M:
             raise ValueError(f"{name} has fewer than M entries")
-    C = M if chunk_rows <= 0 or chunk_rows >= M else int(chunk_rows)
-    need = mosaic_logits_argmax_lse_workspace_bytes(C, V)
+    need = mosaic_logits_argmax_lse_workspace_bytes(M, chunk_rows, V)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _check(lib.mosaic_masked_logits_argmax_lse(
@@ -303,8 +334,9 @@ def mosaic_quantize_rows_fp8(X: torch.Tensor, row_idx: torch.Tensor | None = Non
     return q, scale
 
 
-def mosaic_logits_fp8_workspace_bytes(rows: int, d: int) -> int:
-    n = int(lib.mosaic_logits_fp8_workspace_bytes(int(rows), int(d)))
+def mosaic_logits_fp8_workspace_bytes(M: int, chunk_rows: int, d: int) -> int:
+    """Workspace bytes mosaic_masked_logits_fp8 needs for M rows in chunks of chunk_rows."""
+    n = int(lib.mosaic_logits_fp8_workspace_bytes(int(M), int(chunk_rows), int(d)))
     if n < 0:
         raise ValueError("workspace size overflows")
     return n
@@ -326,9 +358,8 @@ def mosaic_masked_logits_fp8(H: torch.Tensor, idx: torch.Tensor, Wq: torch.Tenso
         out = torch.empty((M, V), dtype=torch.bfloat16, device=H.device)
     elif out.numel() < M * V:
         raise ValueError("out is smaller than M * V")
-    C = M if chunk_rows <= 0 or chunk_rows >= M else int(chunk_rows)
     if workspace is None:
-        workspace = torch.empty(max(16, mosaic_logits_fp8_workspace_bytes(C, d)), dtype=torch.uint8,
+        workspace = torch.empty(max(16, mosaic_logits_fp8_workspace_bytes(M, chunk_rows, d)), dtype=torch.uint8,
                                 device=H.device)
     _check(lib.mosaic_masked_logits_fp8(_dev(H, "H", torch.bfloat16), L, d, _dev(idx, "idx", torch.int32), M,
                                         _dev(Wq, "Wq", torch.uint8), _dev(w_scale, "w_scale", torch.float32), V,

@@ -98,19 +98,36 @@ def test_empty_problems_are_ok_without_pointers(m):
     assert _logits(m, V=0, H=None, W=None, idx=None, out=None) == 0
 
 
+def test_compact_workspace_bytes(m):
+    f = m.lib.mosaic_mask_compact_workspace_bytes
+    for L in (0, 1, 8192, 131072, 2**31 - 1):
+        assert f(L) == 0
+    assert m.mosaic_mask_compact_workspace_bytes(65536) == 0
+
+
 def test_compact_validation(m):
     L = m.lib
-    assert L.mosaic_mask_compact(A16, -1, 0, A16, A16, None) == 1
-    assert L.mosaic_mask_compact(None, 10, 0, A16, A16, None) == 1
-    assert L.mosaic_mask_compact(A16, 10, 0, None, A16, None) == 1
-    assert L.mosaic_mask_compact(A16, 10, 0, A16, None, None) == 1
-    assert L.mosaic_mask_compact(A16, 2**31, 0, A16, A16, None) == 2
-    assert L.mosaic_mask_compact_flags(None, 10, A16, A16, None) == 1
-    assert L.mosaic_mask_compact_flags(A16, 10, A16, None, None) == 1
-    assert L.mosaic_mask_compact_batched(A16, 10, A16, 0, 0, A16, A16, None) == 1
-    assert L.mosaic_mask_compact_batched(A16, 10, None, 2, 0, A16, A16, None) == 1
-    assert L.mosaic_mask_compact_batched(A16, 10, A16, 2, 0, A16, None, None) == 1
-    assert L.mosaic_mask_compact_batched(A16, 2**31, A16, 2, 0, A16, A16, None) == 2
+    assert L.mosaic_mask_compact(A16, -1, 0, A16, A16, None, 0, None) == 1
+    assert L.mosaic_mask_compact(None, 10, 0, A16, A16, None, 0, None) == 1
+    assert L.mosaic_mask_compact(A16, 10, 0, None, A16, None, 0, None) == 1
+    assert L.mosaic_mask_compact(A16, 10, 0, A16, None, None, 0, None) == 1
+    assert L.mosaic_mask_compact(A16, 2**31, 0, A16, A16, None, 0, None) == 2
+    assert L.mosaic_mask_compact_flags(None, 10, A16, A16, None, 0, None) == 1
+    assert L.mosaic_mask_compact_flags(A16, 10, A16, None, None, 0, None) == 1
+    assert L.mosaic_mask_compact_batched(A16, 10, A16, 0, 0, A16, A16, None, 0, None) == 1
+    assert L.mosaic_mask_compact_batched(A16, 10, None, 2, 0, A16, A16, None, 0, None) == 1
+    assert L.mosaic_mask_compact_batched(A16, 10, A16, 2, 0, A16, None, None, 0, None) == 1
+    assert L.mosaic_mask_compact_batched(A16, 2**31, A16, 2, 0, A16, A16, None, 0, None) == 2
+
+
+def test_compact_rejects_claimed_bytes_without_a_workspace(m):
+    # bytes claimed for a NULL workspace are an inconsistent argument pair
+    L = m.lib
+    assert L.mosaic_mask_compact(A16, 10, 0, A16, A16, None, 64, None) == 1
+    assert L.mosaic_mask_compact_flags(A16, 10, A16, A16, None, 64, None) == 1
+    assert L.mosaic_mask_compact_batched(A16, 10, A16, 2, 0, A16, A16, None, 64, None) == 1
+    # an empty sequence with a consistent (empty) workspace still validates its pointers
+    assert L.mosaic_mask_compact(None, 0, 0, None, None, None, 0, None) == 1
 
 
 def test_binding_rejects_host_tensors(m):
@@ -138,11 +155,22 @@ def _argmax_lse(m, H=A16, L=100, d=64, idx=A16, M=10, W=A16, V=50, out=None, C=0
 
 def test_argmax_lse_workspace_bytes(m):
     f = m.lib.mosaic_logits_argmax_lse_workspace_bytes
-    assert f(4096, 126464) == 12 * 494 * 4096
-    assert f(10, 1) == 120 and f(10, 256) == 120 and f(10, 257) == 240
-    assert f(0, 100) == 0
-    assert f(-1, 10) == -1 and f(10, -1) == -1
-    assert f(2**62, 2**20) == -1
+    # (M, chunk_rows, V): sized by the largest chunk
+    assert f(29491, 4096, 126464) == 12 * 494 * 4096
+    assert f(4096, 0, 126464) == 12 * 494 * 4096
+    assert f(10, 0, 1) == 120 and f(10, 0, 256) == 120 and f(10, 0, 257) == 240
+    assert f(10, 100, 256) == 120                       # chunk_rows >= M: one chunk of M rows
+    assert f(1000, 100, 256) == 1200 and f(1001, 100, 256) == 1200
+    assert f(0, 0, 100) == 0 and f(0, 7, 100) == 0
+    assert f(-1, 0, 10) == -1 and f(10, 0, -1) == -1
+    assert f(2**62, 0, 2**20) == -1
+    assert m.mosaic_logits_argmax_lse_workspace_bytes(1000, 100, 256) == 1200
+
+
+def test_argmax_lse_rejects_a_workspace_one_byte_short(m):
+    for M, C, V in ((10, 0, 50), (1000, 100, 300), (1001, 100, 300), (37, 5, 513)):
+        need = m.mosaic_logits_argmax_lse_workspace_bytes(M, C, V)
+        assert _argmax_lse(m, M=M, C=C, V=V, wsb=need - 1) == 1
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -198,11 +226,20 @@ def test_lazy_chunk_rows_errors(m):
 
 def test_fp8_workspace_bytes(m):
     f = m.lib.mosaic_logits_fp8_workspace_bytes
-    assert f(4096, 4096) == 4096 * 4096 + 4 * 4096
-    assert f(3, 10) == 32 + 12
-    assert f(0, 10) == 0
-    assert f(-1, 10) == -1 and f(10, -1) == -1
-    assert f(2**62, 2**10) == -1
+    # (M, chunk_rows, d): sized by the largest chunk
+    assert f(4096, 0, 4096) == 4096 * 4096 + 4 * 4096
+    assert f(29491, 4096, 4096) == 4096 * 4096 + 4 * 4096
+    assert f(3, 0, 10) == 32 + 12
+    assert f(30, 3, 10) == 32 + 12 and f(31, 3, 10) == 32 + 12
+    assert f(0, 0, 10) == 0
+    assert f(-1, 0, 10) == -1 and f(10, 0, -1) == -1
+    assert f(2**62, 0, 2**10) == -1
+
+
+def test_fp8_rejects_a_workspace_one_byte_short(m):
+    for M, C, d in ((10, 0, 128), (1000, 100, 256), (1001, 100, 128)):
+        need = m.mosaic_logits_fp8_workspace_bytes(M, C, d)
+        assert _lf8(m, M=M, C=C, d=d, wb=need - 1) == 1
 
 
 def _quant(m, X=A16, n=100, d=64, i=1, ridx=None, rows=10, q=A16, sc=A16):

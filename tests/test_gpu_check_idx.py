@@ -31,12 +31,12 @@ def _setup(seed, L=300, d=256, V=700, M=100):
 
 
 @pytest.mark.parametrize("bad", [-1, "L"])
-def test_check_rejects_out_of_range(m, monkeypatch, bad):
+def test_check_rejects_out_of_range(m, lib_env, bad):
     wl, H, idx, W = _setup(41)
     L, V, M = H.shape[0], W.shape[0], idx.numel()
     bad_idx = idx.clone()
     bad_idx[M // 2] = L if bad == "L" else -1
-    monkeypatch.setenv("MOSAIC_CHECK_IDX", "1")
+    lib_env("MOSAIC_CHECK_IDX", "1")
     out = torch.full((M, V), 3.0, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(m.MosaicError) as e:
         m.mosaic_masked_logits(H, bad_idx, W, out=out)
@@ -51,11 +51,11 @@ def test_check_rejects_out_of_range(m, monkeypatch, bad):
     assert torch.all(out == 3.0) and torch.all(rmax == 7.0)
 
 
-def test_check_passes_valid_indices(m, monkeypatch):
+def test_check_passes_valid_indices(m, lib_env):
     wl, H, idx, W = _setup(42)
     ref = m.mosaic_masked_logits(H, idx, W)
     ref_c = m.mosaic_masked_logits_argmax_lse(H, idx, W)
-    monkeypatch.setenv("MOSAIC_CHECK_IDX", "1")
+    lib_env("MOSAIC_CHECK_IDX", "1")
     got = m.mosaic_masked_logits(H, idx, W, chunk_rows=33)
     got_c = m.mosaic_masked_logits_argmax_lse(H, idx, W)
     torch.cuda.synchronize()

@@ -101,3 +101,22 @@ def test_compact_ragged_workload(m):
     torch.cuda.synchronize()
     assert np.array_equal(off.cpu().numpy(), want_off)
     assert np.array_equal(idx[:want_off[-1]].cpu().numpy(), want_idx)
+
+
+def test_compact_with_a_caller_workspace(m):
+    # a caller that passes the workspace the query asks for (here 0 bytes, any buffer)
+    # gets the same lists as one that passes none
+    wl = inputs.make_workload("llada_step", with_weights=False)
+    assert m.mosaic_mask_compact_workspace_bytes(wl.L) == 0
+    ws = torch.empty(64, dtype=torch.uint8, device=DEV)
+    want = oracle.mask_compact(wl.tokens, wl.mask_id)
+    idx, cnt = m.mosaic_mask_compact(wl.tokens.to(DEV), wl.mask_id, workspace=ws)
+    flags = torch.from_numpy((wl.tokens.numpy() == wl.mask_id).astype(np.uint8)).to(DEV)
+    idx_f, cnt_f = m.mosaic_mask_compact_flags(flags, workspace=ws)
+    so = torch.tensor([0, wl.L // 2, wl.L], dtype=torch.int32, device=DEV)
+    idx_b, off_b = m.mosaic_mask_compact_batched(wl.tokens.to(DEV), so, wl.mask_id, workspace=ws)
+    torch.cuda.synchronize()
+    c = int(cnt.item())
+    assert c == want.size and np.array_equal(idx[:c].cpu().numpy(), want)
+    assert int(cnt_f.item()) == c and np.array_equal(idx_f[:c].cpu().numpy(), want)
+    assert int(off_b[-1].item()) == c and np.array_equal(idx_b[:c].cpu().numpy(), want)

@@ -79,8 +79,10 @@ def test_ragged_full_batch(m):
     H, W, idx, M, out = _step(m, wl)
     want_idx, want_off = oracle.mask_compact_batched(wl.tokens, wl.seq_offsets, wl.mask_id)
     assert M == want_off[-1] and np.array_equal(idx[:M].cpu().numpy(), want_idx)
-    # two sampled rows per sequence: its first and last masked row
-    rows = np.unique(np.concatenate([want_off[:-1], want_off[1:] - 1]).astype(np.int64))
+    # each sequence's first and last masked row, rows around 256-row tile boundaries and
+    # seeded random rows inside the sequences (CSR output order)
+    rows = np.unique(np.concatenate([want_off[:-1], want_off[1:] - 1,
+                                     sample_rows(M, 0, 24, seed=M)]).astype(np.int64))
     ref = oracle.masked_logits(wl.H, want_idx, wl.W, rows=rows)
     assert_close(out[torch.from_numpy(rows).to(DEV)], ref, "ragged sampled rows")
     other = m.mosaic_masked_logits(H, idx, W, M=M, chunk_rows=4096)
@@ -88,21 +90,47 @@ def test_ragged_full_batch(m):
     assert torch.equal(other, out)
 
 
-def test_one_hot_full_shape_bit_exact(m):
-    # W[v, k] = [k == v mod d]: every logit is an exact copy of a gathered H element
-    wl = inputs.make_workload("long_logits")
+def _masked_rows(m, wl):
+    tok = wl.tokens.to(DEV)
+    if wl.seq_offsets is not None:
+        idx, off = m.mosaic_mask_compact_batched(tok, wl.seq_offsets.to(DEV), wl.mask_id)
+        return idx, int(off[-1].item())
+    idx, cnt = m.mosaic_mask_compact(tok, wl.mask_id)
+    return idx, int(cnt.item())
+
+
+@pytest.mark.parametrize("name", ["long_logits", "long_ffn", "ragged", "llada_step"])
+def test_one_hot_w_full_shape_bit_exact(m, name):
+    # W[v, k] = [k == v mod d]: every logit is an exact copy of a gathered H element, so
+    # every element of the full-size output pins the gather addressing bit for bit
+    wl = inputs.make_workload(name)
     d, V = wl.d, wl.V
     W1 = inputs.one_hot_rows(V, d).to(DEV)
-    tok = wl.tokens.to(DEV)
-    idx, cnt = m.mosaic_mask_compact(tok, wl.mask_id)
-    M = int(cnt.item())
+    idx, M = _masked_rows(m, wl)
     H = wl.H.to(DEV)
     out = m.mosaic_masked_logits(H, idx, W1, M=M, chunk_rows=wl.chunk_rows)
     cols = torch.arange(V, device=DEV) % d
     for r0 in range(0, M, 2048):
         r1 = min(M, r0 + 2048)
         want = H[idx[r0:r1].long()][:, cols]
-        assert torch.equal(out[r0:r1], want), r0
+        assert torch.equal(out[r0:r1], want), (name, r0)
+
+
+@pytest.mark.parametrize("name", ["long_logits", "long_ffn", "ragged", "llada_step"])
+def test_one_hot_h_full_shape_bit_exact(m, name):
+    # H[p, k] = [k == p mod d]: row i of the output is column idx[i] mod d of W, exactly
+    wl = inputs.make_workload(name)
+    d, V = wl.d, wl.V
+    idx, M = _masked_rows(m, wl)
+    H1 = inputs.one_hot_rows(wl.L, d).to(DEV)
+    W = wl.W.to(DEV)
+    out = m.mosaic_masked_logits(H1, idx, W, M=M, chunk_rows=wl.chunk_rows)
+    Wt = W.T.contiguous()                              # [d, V]: row k is column k of W
+    for r0 in range(0, M, 2048):
+        r1 = min(M, r0 + 2048)
+        want = Wt[(idx[r0:r1].long() % d)]
+        assert torch.equal(out[r0:r1], want), (name, r0)
+    del Wt
 
 
 def test_integer_inputs_full_shape_bit_exact(m):

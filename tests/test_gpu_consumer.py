@@ -187,7 +187,7 @@ def test_other_workloads_sampled_rows(m, name):
 
 
 @pytest.mark.parametrize("L,d,V,M,C", [CASES[0], CASES[2], CASES[4], CASES[6]])
-def test_mfma_forms_match(m, monkeypatch, L, d, V, M, C):
+def test_mfma_forms_match(m, lib_env, L, d, V, M, C):
     # the 32 x 32 x 16 MFMA form of the fused kernel (variant=16) against the default
     # 16 x 16 x 32 form: same fp32 logits, so the row max, argmax and stored logits are
     # identical; the exp sums are added in another order (oracle bound only)
@@ -196,10 +196,10 @@ def test_mfma_forms_match(m, monkeypatch, L, d, V, M, C):
     H, W = wl.H.to(DEV), wl.W.to(DEV)
     got = m.mosaic_masked_logits_argmax_lse(H, idx_d, W, chunk_rows=C, store_logits=True)
     only = m.mosaic_masked_logits_argmax_lse(H, idx_d, W, chunk_rows=C)
-    monkeypatch.setenv("MOSAIC_TUNE", "variant=16")
+    lib_env("MOSAIC_TUNE", "variant=16")
     ref = m.mosaic_masked_logits_argmax_lse(H, idx_d, W, chunk_rows=C, store_logits=True)
     torch.cuda.synchronize()
-    monkeypatch.delenv("MOSAIC_TUNE")
+    lib_env("MOSAIC_TUNE", None)
     assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
     assert torch.equal(got[3], ref[3])
     for x, y in zip(only[:3], got[:3]):

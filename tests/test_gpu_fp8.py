@@ -66,7 +66,7 @@ def test_parity_random(m, L, d, V, M, C):
     assert_close(out, ref, f"fp8 {L},{d},{V},{M},{C}")
 
 
-def test_chunked_waves_and_determinism(m, monkeypatch):
+def test_chunked_waves_and_determinism(m, lib_env):
     wl = inputs.make_random(55, L=1500, d=256, V=2000, M=1100, dtype="bf16")
     idx_d = torch.from_numpy(oracle.mask_compact(wl.tokens, wl.mask_id)).to(DEV)
     H = wl.H.to(DEV)
@@ -75,10 +75,10 @@ def test_chunked_waves_and_determinism(m, monkeypatch):
     for C in (1, 64, 255, 256, 300, 1099, -1):
         assert torch.equal(m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws, chunk_rows=C), ref), C
     for tune in ("waves=4",):
-        monkeypatch.setenv("MOSAIC_TUNE", tune)
+        lib_env("MOSAIC_TUNE", tune)
         assert torch.equal(m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws), ref), tune
         assert torch.equal(m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws, chunk_rows=300), ref), tune
-    monkeypatch.delenv("MOSAIC_TUNE")
+    lib_env("MOSAIC_TUNE", None)
     torch.cuda.synchronize()
 
 
@@ -133,13 +133,13 @@ LOWM_CASES = [
 
 
 @pytest.mark.parametrize("L,d,V,M", LOWM_CASES)
-def test_lowm_kernel_parity_and_bit_identity(m, monkeypatch, L, d, V, M):
+def test_lowm_kernel_parity_and_bit_identity(m, lib_env, L, d, V, M):
     wl = inputs.make_random(L + 7 * d + V + M, L=L, d=d, V=V, M=M, dtype="bf16")
     idx = oracle.mask_compact(wl.tokens, wl.mask_id)
     H, idx_d = wl.H.to(DEV), torch.from_numpy(idx).to(DEV)
     Wq, ws = m.mosaic_quantize_rows_fp8(wl.W.to(DEV))
     out = m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws)
-    monkeypatch.setenv("MOSAIC_TUNE", "fp8lowm=0")          # the tiled FP8 kernel
+    lib_env("MOSAIC_TUNE", "fp8lowm=0")          # the tiled FP8 kernel
     tiled = m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws)
     torch.cuda.synchronize()
     assert torch.equal(out, tiled)

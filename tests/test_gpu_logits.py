@@ -80,9 +80,9 @@ LOWM_CASES = [
 
 @pytest.mark.parametrize("variant", [6, 20])
 @pytest.mark.parametrize("dt_out,L,d,V,M", LOWM_CASES)
-def test_parity_lowm(m, monkeypatch, variant, dt_out, L, d, V, M):
+def test_parity_lowm(m, lib_env, variant, dt_out, L, d, V, M):
     # both low-M streaming kernels: private H copies per wave (6) and a workgroup-shared H tile (20)
-    monkeypatch.setenv("MOSAIC_TUNE", f"variant={variant}")
+    lib_env("MOSAIC_TUNE", f"variant={variant}")
     assert m.mosaic_logits_variant(M, V, d, torch.bfloat16, TD[dt_out]) == variant
     wl = inputs.make_random(L + d + V + M, L=L, d=d, V=V, M=M, dtype="bf16")
     idx, idx_d = _gpu_idx(wl)
@@ -99,7 +99,7 @@ def test_parity_lowm(m, monkeypatch, variant, dt_out, L, d, V, M):
                                        (2048, 128, 32768, "bf16"),
                                        # low-M shapes with several blocks per wave
                                        (20, 64, 131584, "bf16"), (64, 128, 40000, "f32"), (20, 64, 300000, "bf16")])
-def test_bf16_variants_bit_identical(m, monkeypatch, M, d, V, out):
+def test_bf16_variants_bit_identical(m, lib_env, M, d, V, out):
     # every bf16 MFMA variant accumulates each output in the same MFMA k order
     wl = inputs.make_random(M + d + V, L=max(M, 300), d=d, V=V, M=M, dtype="bf16")
     _, idx_d = _gpu_idx(wl)
@@ -110,13 +110,13 @@ def test_bf16_variants_bit_identical(m, monkeypatch, M, d, V, out):
             continue
         if v in (6, 20) and M > 64:
             continue
-        monkeypatch.setenv("MOSAIC_TUNE", f"variant={v}")
+        lib_env("MOSAIC_TUNE", f"variant={v}")
         if out == "bf16" or v < 15:            # the deferred-store kernels write bf16 only
             assert m.mosaic_logits_variant(M, V, d, torch.bfloat16, TD[out]) == v
         got = m.mosaic_masked_logits(H, idx_d, W, out_dtype=TD[out])
         torch.cuda.synchronize()
         assert torch.equal(got, ref), v
-    monkeypatch.delenv("MOSAIC_TUNE")
+    lib_env("MOSAIC_TUNE", None)
 
 
 @pytest.mark.parametrize("d,V,M", [(4096, 1000, 300), (512, 1001, 600), (72, 100, 50)])
