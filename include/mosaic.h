@@ -190,6 +190,31 @@ mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_
                                                 void *workspace, int64_t workspace_bytes,
                                                 void *stream);
 
+/* Size of the library-owned device array behind mosaic_masked_logits_argmax_lse_noalloc
+ * (32 MiB; each device that runs the call holds one until the process ends). */
+#define MOSAIC_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): mosaic_masked_logits_argmax_lse with
+ * no workspace argument and no allocation of any kind.  The per-row partials of a chunk
+ * go to a library-owned device array of MOSAIC_NOALLOC_SCRATCH_BYTES bytes per device.
+ *   Arguments, results and errors as for mosaic_masked_logits_argmax_lse, except:
+ *   - a call whose chunks need more than the array,
+ *     mosaic_logits_argmax_lse_workspace_bytes(M, chunk_rows, V) > MOSAIC_NOALLOC_SCRATCH_BYTES
+ *     (about 5,600 rows per chunk at V = 126464), returns MOSAIC_ERR_UNSUPPORTED and
+ *     enqueues nothing: pass a smaller chunk_rows;
+ *   - the MOSAIC_CHECK_IDX debug check is not made (it would allocate and synchronise);
+ *   - every call on one device shares the array, so calls that overlap in time on one
+ *     device (on different streams, or from several host threads) race and their results
+ *     are undefined: serialise them.  Calls in order on one stream are safe. */
+mosaic_status_t mosaic_masked_logits_argmax_lse_noalloc(const void *H, int64_t L, int64_t d,
+                                                        const int32_t *idx, int64_t M,
+                                                        const void *W, int64_t V,
+                                                        void *out, int64_t chunk_rows,
+                                                        mosaic_dtype_t in_dtype, mosaic_dtype_t out_dtype,
+                                                        float *row_max, int32_t *row_argmax, float *row_lse,
+                                                        void *stream);
+
 /* Workspace bytes of mosaic_masked_logits_argmax_lse for M rows in chunks of
  * chunk_rows over V vocabulary entries: 12 * ceil(V / 256) * C, with C the rows of the
  * largest chunk (three 4-byte partials per row and 256-entry tile; one chunk's partials

@@ -180,6 +180,33 @@ int pick_variant(int64_t M, int64_t V, int64_t d, mosaic_dtype_t in, mosaic_dtyp
     return -1;
 }
 
+// Scratch of mosaic_masked_logits_argmax_lse_noalloc: the per-(row, vocabulary tile)
+// partials of one chunk.  Each device the library runs on holds its own copy of this array
+// until the process ends; host code uses the device address from hipGetSymbolAddress,
+// taken once per device with that device current, never the array's name.
+static __device__ __attribute__((aligned(256))) char scratch[MOSAIC_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::map<int, void *> g_scratch_ptr;
+
+// The current device's address of `scratch` (looked up on the first call on a device).
+mosaic_status_t noalloc_scratch(void **ptr)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return MOSAIC_ERR_DEVICE;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch_ptr.find(dev);
+    if (it == g_scratch_ptr.end()) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return MOSAIC_ERR_DEVICE;
+        it = g_scratch_ptr.emplace(dev, p).first;
+    }
+    *ptr = it->second;
+    return MOSAIC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -384,11 +411,14 @@ int64_t mosaic_logits_argmax_lse_workspace_bytes(int64_t M, int64_t chunk_rows, 
     return argmax_lse_partials_bytes(largest_chunk_rows(M, chunk_rows), V);
 }
 
-mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_t d, const int32_t *idx, int64_t M,
-                                                const void *W, int64_t V, void *out, int64_t chunk_rows,
-                                                mosaic_dtype_t in_dtype, mosaic_dtype_t out_dtype, float *row_max,
-                                                int32_t *row_argmax, float *row_lse, void *workspace,
-                                                int64_t workspace_bytes, void *stream)
+// Shared body of the two consumer entry points.  noalloc: the partials go to this
+// library's scratch array (workspace and workspace_bytes are ignored), and the idx debug
+// check, which allocates and synchronises, is not made.
+static mosaic_status_t argmax_lse_impl(const void *H, int64_t L, int64_t d, const int32_t *idx, int64_t M,
+                                       const void *W, int64_t V, void *out, int64_t chunk_rows,
+                                       mosaic_dtype_t in_dtype, mosaic_dtype_t out_dtype, float *row_max,
+                                       int32_t *row_argmax, float *row_lse, void *workspace,
+                                       int64_t workspace_bytes, bool noalloc, void *stream)
 {
     if (M < 0 || V < 0 || L < 0 || d < 0)
         return MOSAIC_ERR_INVALID_ARG;
@@ -402,9 +432,9 @@ mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_
         return MOSAIC_ERR_UNSUPPORTED;
     if (d % 64 != 0 || d > (1 << 22))
         return MOSAIC_ERR_UNSUPPORTED;
-    if (!H || !W || !idx || !row_max || !row_argmax || !row_lse || !workspace || L == 0 || d == 0)
+    if (!H || !W || !idx || !row_max || !row_argmax || !row_lse || (!noalloc && !workspace) || L == 0 || d == 0)
         return MOSAIC_ERR_INVALID_ARG;
-    if (!aligned16(H) || !aligned16(W) || (out && !aligned16(out)) || !aligned16(workspace) ||
+    if (!aligned16(H) || !aligned16(W) || (out && !aligned16(out)) || (!noalloc && !aligned16(workspace)) ||
         ((uintptr_t)idx & 3u) || ((uintptr_t)row_max & 3u) || ((uintptr_t)row_argmax & 3u) ||
         ((uintptr_t)row_lse & 3u))
         return MOSAIC_ERR_INVALID_ARG;
@@ -417,16 +447,29 @@ mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_
     if (C > kMaxPos || !mosaic::gather_gemm_grid_fits(mosaic::kVariantBf16DeferS4I8, C, V))
         return MOSAIC_ERR_UNSUPPORTED;
     const int64_t need = argmax_lse_partials_bytes(C, V);
-    if (need < 0 || workspace_bytes < need)
+    if (need < 0)
         return MOSAIC_ERR_INVALID_ARG;
-    // workspace: pmax, parg, psum, each [ceil(V/256)][C] 4-byte words
+    if (noalloc) {
+        if (need > (int64_t)MOSAIC_NOALLOC_SCRATCH_BYTES)
+            return MOSAIC_ERR_UNSUPPORTED;     // the partials of one chunk exceed the scratch array
+        const mosaic_status_t sc = noalloc_scratch(&workspace);
+        if (sc != MOSAIC_OK)
+            return sc;
+    } else if (workspace_bytes < need) {
+        return MOSAIC_ERR_INVALID_ARG;
+    }
+    // workspace: pmax, parg, psum, each [ceil(V/256)][C] 4-byte words; every entry is written
+    // by a chunk's GEMM launch before that chunk's finish kernel reads it, so nothing needs
+    // clearing
     const int64_t plane = (V + 255) / 256 * C;
     float *pmax = (float *)workspace;
     int32_t *parg = (int32_t *)(pmax + plane);
     float *psum = (float *)(parg + plane);
-    const mosaic_status_t ck = check_idx_if_asked(idx, M, L, (hipStream_t)stream);
-    if (ck != MOSAIC_OK)
-        return ck;
+    if (!noalloc) {
+        const mosaic_status_t ck = check_idx_if_asked(idx, M, L, (hipStream_t)stream);
+        if (ck != MOSAIC_OK)
+            return ck;
+    }
     const Tune t = read_tune();
     const bool m16 = t.variant != mosaic::kVariantBf16DeferS4I8;   // 32 x 32 x 16 form on request
     for (int64_t k = 0; k < K; ++k) {
@@ -440,6 +483,26 @@ mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_
             return MOSAIC_ERR_DEVICE;
     }
     return MOSAIC_OK;
+}
+
+mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_t d, const int32_t *idx, int64_t M,
+                                                const void *W, int64_t V, void *out, int64_t chunk_rows,
+                                                mosaic_dtype_t in_dtype, mosaic_dtype_t out_dtype, float *row_max,
+                                                int32_t *row_argmax, float *row_lse, void *workspace,
+                                                int64_t workspace_bytes, void *stream)
+{
+    return argmax_lse_impl(H, L, d, idx, M, W, V, out, chunk_rows, in_dtype, out_dtype, row_max, row_argmax,
+                           row_lse, workspace, workspace_bytes, false, stream);
+}
+
+mosaic_status_t mosaic_masked_logits_argmax_lse_noalloc(const void *H, int64_t L, int64_t d, const int32_t *idx,
+                                                        int64_t M, const void *W, int64_t V, void *out,
+                                                        int64_t chunk_rows, mosaic_dtype_t in_dtype,
+                                                        mosaic_dtype_t out_dtype, float *row_max,
+                                                        int32_t *row_argmax, float *row_lse, void *stream)
+{
+    return argmax_lse_impl(H, L, d, idx, M, W, V, out, chunk_rows, in_dtype, out_dtype, row_max, row_argmax,
+                           row_lse, nullptr, 0, true, stream);
 }
 
 mosaic_status_t mosaic_quantize_rows_fp8(const void *X, int64_t nsrc, int64_t d, mosaic_dtype_t in_dtype,

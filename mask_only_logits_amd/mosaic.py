@@ -23,6 +23,7 @@ MOSAIC_ERR_UNSUPPORTED = 2
 MOSAIC_ERR_DEVICE = 3
 MOSAIC_F32 = 0
 MOSAIC_BF16 = 1
+MOSAIC_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Every symbol include/mosaic.h declares.
 EXPORTS = (
@@ -36,6 +37,7 @@ EXPORTS = (
     "mosaic_logits_bytes",
     "mosaic_logits_variant",
     "mosaic_masked_logits_argmax_lse",
+    "mosaic_masked_logits_argmax_lse_noalloc",
     "mosaic_logits_argmax_lse_workspace_bytes",
     "mosaic_lazy_chunk_rows",
     "mosaic_quantize_rows_fp8",
@@ -78,6 +80,8 @@ def _load() -> ctypes.CDLL:
     lib.mosaic_logits_variant.argtypes = [i64, i64, i64, st, st]
     lib.mosaic_masked_logits_argmax_lse.restype = st
     lib.mosaic_masked_logits_argmax_lse.argtypes = [p, i64, i64, p, i64, p, i64, p, i64, st, st, p, p, p, p, i64, p]
+    lib.mosaic_masked_logits_argmax_lse_noalloc.restype = st
+    lib.mosaic_masked_logits_argmax_lse_noalloc.argtypes = [p, i64, i64, p, i64, p, i64, p, i64, st, st, p, p, p, p]
     lib.mosaic_logits_argmax_lse_workspace_bytes.restype = i64
     lib.mosaic_logits_argmax_lse_workspace_bytes.argtypes = [i64, i64, i64]
     lib.mosaic_quantize_rows_fp8.restype = st
@@ -311,6 +315,35 @@ def mosaic_masked_logits_argmax_lse(H: torch.Tensor, idx: torch.Tensor, W: torch
         _dev(row_max, "row_max", torch.float32), _dev(row_argmax, "row_argmax", torch.int32),
         _dev(row_lse, "row_lse", torch.float32), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         _stream(stream)), "mosaic_masked_logits_argmax_lse")
+    return row_max, row_argmax, row_lse, out
+
+
+def mosaic_masked_logits_argmax_lse_noalloc(H: torch.Tensor, idx: torch.Tensor, W: torch.Tensor,
+                                            row_max: torch.Tensor, row_argmax: torch.Tensor,
+                                            row_lse: torch.Tensor, M: int | None = None, chunk_rows: int = 0,
+                                            out: torch.Tensor | None = None, stream=None):
+    """mosaic_masked_logits_argmax_lse without a workspace: the library allocates nothing
+    and the partials use its own per-device scratch array.  The caller passes every
+    output (row_max float32 [M], row_argmax int32 [M], row_lse float32 [M], and `out`
+    [M, V] bf16 when the logits are wanted); this wrapper allocates nothing either."""
+    if H.dim() != 2 or W.dim() != 2 or H.shape[1] != W.shape[1]:
+        raise ValueError("H must be [L, d] and W [V, d]")
+    L, d = H.shape
+    V = W.shape[0]
+    M = idx.numel() if M is None else int(M)
+    if M > idx.numel():
+        raise ValueError("M exceeds the length of idx")
+    if out is not None and out.numel() < M * V:
+        raise ValueError("out is smaller than M * V")
+    for name, t in (("row_max", row_max), ("row_argmax", row_argmax), ("row_lse", row_lse)):
+        if t.numel() < M:
+            raise ValueError(f"{name} has fewer than M entries")
+    _check(lib.mosaic_masked_logits_argmax_lse_noalloc(
+        _dev(H, "H"), L, d, _dev(idx, "idx", torch.int32), M, _dev(W, "W"), V,
+        _dev(out, "out") if out is not None else None, int(chunk_rows), _dtype_code(H.dtype),
+        _dtype_code(out.dtype) if out is not None else MOSAIC_BF16,
+        _dev(row_max, "row_max", torch.float32), _dev(row_argmax, "row_argmax", torch.int32),
+        _dev(row_lse, "row_lse", torch.float32), _stream(stream)), "mosaic_masked_logits_argmax_lse_noalloc")
     return row_max, row_argmax, row_lse, out
 
 

@@ -283,3 +283,33 @@ def test_logits_fp8_validation(m, kw, status):
 
 def test_logits_fp8_empty_is_ok(m):
     assert _lf8(m, M=0, H=None, idx=None, Wq=None, ws=None, out=None, w=None, wb=0) == 0
+
+
+def _noalloc(m, H=A16, L=100, d=64, idx=A16, M=10, W=A16, V=50, out=None, C=0, i=1, o=1,
+             rmax=A16, rarg=A16, rlse=A16):
+    return m.lib.mosaic_masked_logits_argmax_lse_noalloc(H, L, d, idx, M, W, V, out, C, i, o, rmax, rarg, rlse,
+                                                         None)
+
+
+def test_noalloc_rejects_chunks_beyond_its_scratch(m):
+    # 12 * ceil(V / 256) * C bytes of partials per chunk must fit the 32 MiB array
+    V = 126464
+    fits = m.MOSAIC_NOALLOC_SCRATCH_BYTES // (12 * 494)
+    assert m.mosaic_logits_argmax_lse_workspace_bytes(fits, 0, V) <= m.MOSAIC_NOALLOC_SCRATCH_BYTES
+    assert m.mosaic_logits_argmax_lse_workspace_bytes(fits + 1, 0, V) > m.MOSAIC_NOALLOC_SCRATCH_BYTES
+    assert _noalloc(m, L=40000, d=4096, M=fits + 1, V=V) == 2              # one chunk too large
+    assert _noalloc(m, L=40000, d=4096, M=29491, C=fits + 1, V=V) == 2     # chunks too large
+    assert _noalloc(m, L=40000, d=4096, M=30000, C=6000, V=V) == 2
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), 1), (dict(V=0), 1), (dict(i=0), 2), (dict(d=72), 2), (dict(out=A16, o=0), 2),
+    (dict(H=None), 1), (dict(W=None), 1), (dict(idx=None), 1), (dict(rmax=None), 1),
+    (dict(H=A8), 1), (dict(rlse=A16 + 2), 1), (dict(L=2**31), 2),
+])
+def test_noalloc_validation(m, kw, status):
+    assert _noalloc(m, **kw) == status
+
+
+def test_noalloc_empty_is_ok_without_pointers(m):
+    assert _noalloc(m, M=0, H=None, W=None, idx=None, rmax=None, rarg=None, rlse=None) == 0
