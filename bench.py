@@ -47,7 +47,7 @@ METRIC = "mask-only logits TFLOP/s (2·M·d·V) and % bf16 MFMA peak at L=32k, d
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
-LOWM_VARIANTS = (6, 20)        # the W-streaming low-M kernels: HBM-bound
+LOWM_VARIANTS = (20,)
 WARMUP_MIN_STEPS = 3
 WARMUP_MIN_SECONDS = 0.15
 
@@ -87,8 +87,10 @@ def _profile_tag(workload: str, path: str) -> str:
 
 
 def measured_traffic(workload: str, path: str = "logits", prof_dir: str | None = None):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; else None."""
+    """L2-miss (L2-to-fabric) bytes per GEMM launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None.  FETCH_SIZE and
+    WRITE_SIZE count what the L2 requests from and sends to the fabric: Infinity-Cache
+    hits included, so this is an upper bound on HBM bytes, not HBM bytes."""
     fname = os.path.join(prof_dir or os.path.join(ROOT, "profiles"),
                          f"traffic_gather_gemm_{_profile_tag(workload, path)}.json")
     try:
@@ -250,8 +252,9 @@ def summarize_profile(root: str, workload: str, copy_mib: int, path: str = "logi
                    "copy_probe_bytes": known}
         with open(os.path.join(prof, f"traffic_gather_gemm_{tag}.json"), "w", encoding="utf-8") as fh:
             json.dump(traffic, fh, indent=1)
-        lines.append(f"traffic per GEMM launch (scaled by the copy probe): fetch {fetch / 1e9:.3f} GB, "
-                     f"write {write / 1e9:.3f} GB (scales {f_scale:.4f}, {w_scale:.4f})")
+        lines.append(f"L2-miss (L2-to-fabric, Infinity-Cache hits included) traffic per GEMM launch, scaled by "
+                     f"the copy probe: fetch {fetch / 1e9:.3f} GB, write {write / 1e9:.3f} GB "
+                     f"(scales {f_scale:.4f}, {w_scale:.4f})")
     out = os.path.join(prof, f"gather_gemm_{tag}_rocprof.md")
     with open(out, "w", encoding="utf-8") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -437,11 +440,11 @@ def main():
         alg_bytes = launches * V * d * esize_in + L * d * esize_in + (L + 2 * M) * V * out.element_size()
     traffic = measured_traffic(args.workload, args.path)
     fp8_lowm = fp8 and rows_per_launch <= 64 and "fp8lowm=0" not in os.environ.get("MOSAIC_TUNE", "")
-    kernel = ("gather_gemm_fp8_lowm_kernel" if fp8_lowm else "gather_gemm_fp8_kernel") if fp8 else "gather_gemm_bf16_defer_kernel" if consumer else {0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel", 6: "gather_gemm_lowm_kernel", 20: "gather_gemm_lowm_shared_kernel",
-              9: "gather_gemm_bf16_persist_kernel", 10: "gather_gemm_bf16_persist_kernel",
-              11: "gather_gemm_bf16_persist_kernel", 15: "gather_gemm_bf16_defer_kernel",
-              16: "gather_gemm_bf16_defer_kernel", 17: "gather_gemm_bf16_defer_kernel",
-              18: "gather_gemm_bf16_defer_kernel", 19: "gather_gemm_bf16_defer_kernel"}.get(variant, "gather_gemm_bf16_kernel")
+    kernel = ("gather_gemm_fp8_lowm_kernel" if fp8_lowm else "gather_gemm_fp8_kernel") if fp8 else \
+        "gather_gemm_bf16_defer_kernel" if consumer else {
+            0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel", 11: "gather_gemm_bf16_persist_kernel",
+            12: "gather_gemm_bf16_kernel", 16: "gather_gemm_bf16_defer_kernel", 19: "gather_gemm_bf16_defer_kernel",
+            20: "gather_gemm_lowm_shared_kernel"}.get(variant, "gather_gemm")
     if variant in LOWM_VARIANTS or fp8_lowm:
         # streaming W is the bound: algorithmic bytes per launch over the launch time
         achieved_gbs = alg_bytes / launches / (gemm_avg / launches / 1e3) / 1e9
@@ -452,7 +455,11 @@ def main():
                     "frac": round(achieved / peak, 4), "traffic": traffic}
     roofline.update({"kernel": kernel, "launch_ms_avg": round(gemm_avg / launches, 4),
                      "algorithmic_bytes_per_launch": int(alg_bytes / launches),
-                     "algorithmic_flop_per_launch": int(flop / launches)})
+                     "algorithmic_flop_per_launch": int(flop / launches),
+                     "traffic_kind": "L2-miss bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a copy "
+                                     "probe; Infinity-Cache hits included, so an upper bound on HBM bytes)",
+                     "traffic_over_algorithmic": (round(traffic / (alg_bytes / launches), 3)
+                                                  if traffic is not None else None)})
     result = {
         "metric": METRIC,
         "value": round(value, 3),

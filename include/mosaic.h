@@ -49,14 +49,22 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* In C++ the enums take int as their fixed underlying type, so that every int a C caller
+ * passes is a valid value (out-of-range codes are then rejected, not undefined). */
+#ifdef __cplusplus
+#define MOSAIC_INT_ENUM : int
+#else
+#define MOSAIC_INT_ENUM
+#endif
+
+typedef enum MOSAIC_INT_ENUM {
     MOSAIC_OK = 0,
     MOSAIC_ERR_INVALID_ARG = 1,   /* null pointer, negative size, misalignment, overflow */
     MOSAIC_ERR_UNSUPPORTED = 2,   /* valid but not supported: dtype pair, d not a multiple of 8 */
     MOSAIC_ERR_DEVICE = 3         /* a HIP launch failed */
 } mosaic_status_t;
 
-typedef enum {
+typedef enum MOSAIC_INT_ENUM {
     MOSAIC_F32 = 0,               /* IEEE binary32 */
     MOSAIC_BF16 = 1               /* bfloat16 (upper half of binary32) */
 } mosaic_dtype_t;

@@ -1374,127 +1374,6 @@ __global__ __launch_bounds__(1024) void logits_reduce_finish_kernel(const float 
 // (rocprofv3, one box), while H, which every step re-reads, keeps the default policy.
 constexpr int kLoadStreaming = 2;
 
-// Low-M gather-GEMM (M <= 32 * AM): the work is streaming W once from HBM.
-//
-// Every wave is an independent stream.  Wave w of the grid owns an equal, contiguous
-// range of vocabulary rows, so every wave streams the same number of W bytes.  It walks
-// its range in blocks of 32 rows (one MFMA A block), each block a full K loop, through
-// a private ring of NSTAGE LDS stages filled by its own global_load_lds DMA: the wave
-// waits on its own vmcnt and needs no workgroup barrier, and its ring keeps running
-// across blocks (the next block's first K tiles are in flight while the current block
-// finishes).  The masked rows (at most 32 * AM) are the MFMA B operand; each wave stages
-// its own copy per K tile from L2 (they are tiny).  Same MFMA, operand roles and k order
-// as the tiled kernel, so the results are bit-identical to it.
-template <int AM, int NSTAGE, bool OUT_BF16>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
-gather_gemm_lowm_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict__ idx, int32_t rows,
-                        const __bf16 *__restrict__ W, int32_t V, int32_t d, void *__restrict__ out,
-                        int64_t ldo)
-{
-    constexpr int BK = 64, ROW_BYTES = 128, CHUNKS = 8, RPI = 8;
-    constexpr int NBK = 8;                        // finished blocks held before a store burst
-    constexpr int W_TILE = 32 * ROW_BYTES;        // 4 KiB: the wave's 32 rows
-    constexpr int H_TILE = 32 * AM * ROW_BYTES;   // 4 or 8 KiB
-    constexpr int STAGE = W_TILE + H_TILE;
-    constexpr int WAVE_LDS = NSTAGE * STAGE;
-    constexpr int LW = W_TILE / 1024, LH = H_TILE / 1024;   // DMA instructions per tile
-    constexpr int T = LW + LH;
-    static_assert(4 * WAVE_LDS <= 160 * 1024, "LDS");
-    static_assert((NSTAGE - 1) * T < 64, "vmcnt");
-
-    __shared__ __attribute__((aligned(1024))) char smem_all[4 * WAVE_LDS];
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    char *smem = smem_all + wave * WAVE_LDS;
-    const int64_t nw = (int64_t)gridDim.x * 4, gw = (int64_t)blockIdx.x * 4 + wave;
-    const int v_lo = lowm::range_bound(gw, nw, V);
-    const int v_hi = lowm::range_bound(gw + 1, nw, V);
-    const int nblocks = (v_hi - v_lo + 31) / 32;
-    const int nk = d / BK;
-    const int ntiles = nblocks * nk;              // flattened (block, k tile) stream
-
-    // DMA lanes: instruction j fills tile rows j*8 + lane/8, physical chunk lane%8.
-    int wch[LW];
-#pragma unroll
-    for (int j = 0; j < LW; ++j)
-        wch[j] = ((lane % CHUNKS) ^ swz<BK>(j * RPI + lane / CHUNKS)) * 16;
-    const char *hsrc[LH];
-#pragma unroll
-    for (int j = 0; j < LH; ++j) {
-        const int r = j * RPI + lane / CHUNKS;
-        hsrc[j] = (const char *)(H + (int64_t)idx[min(r, rows - 1)] * d) + ((lane % CHUNKS) ^ swz<BK>(r)) * 16;
-    }
-
-    auto issue = [&](int so, int g) {
-        const int blk = g / nk, kt = g - blk * nk;
-        const int kb = kt * ROW_BYTES;
-#pragma unroll
-        for (int j = 0; j < LW; ++j) {
-            const int v = min(v_lo + blk * 32 + j * RPI + lane / CHUNKS, v_hi - 1);
-            __builtin_amdgcn_global_load_lds((const void *)((const char *)(W + (int64_t)v * d) + kb + wch[j]),
-                                             (lds_void_t *)(smem + so + j * 1024), 16, 0, kLoadStreaming);
-        }
-#pragma unroll
-        for (int j = 0; j < LH; ++j)
-            __builtin_amdgcn_global_load_lds((const void *)(hsrc[j] + kb),
-                                             (lds_void_t *)(smem + so + W_TILE + j * 1024), 16, 0, 0);
-    };
-
-    // At most n tiles of this wave's DMA still in flight (epilogue stores also count in
-    // vmcnt; they are younger than the loads waited for, so the wait is only stricter).
-    auto wait_tiles = [&](int n) {
-        if (NSTAGE >= 8 && n >= 7) wait_vmcnt<(NSTAGE >= 8 ? 7 : 0) * T>();
-        else if (NSTAGE >= 7 && n >= 6) wait_vmcnt<(NSTAGE >= 7 ? 6 : 0) * T>();
-        else if (NSTAGE >= 6 && n >= 5) wait_vmcnt<(NSTAGE >= 6 ? 5 : 0) * T>();
-        else if (NSTAGE >= 5 && n >= 4) wait_vmcnt<(NSTAGE >= 5 ? 4 : 0) * T>();
-        else if (NSTAGE >= 4 && n >= 3) wait_vmcnt<(NSTAGE >= 4 ? 3 : 0) * T>();
-        else if (NSTAGE >= 3 && n >= 2) wait_vmcnt<(NSTAGE >= 3 ? 2 : 0) * T>();
-        else if (n >= 1) wait_vmcnt<T>();
-        else wait_vmcnt<0>();
-    };
-
-    const int fr = lane & 31, hi = lane >> 5;
-    const int lane_chunk = (hi ^ swz<BK>(fr)) * 16;
-    const int a_addr = fr * ROW_BYTES + lane_chunk;
-    const int b_addr = W_TILE + fr * ROW_BYTES + lane_chunk;
-
-    f32x16_t acc[AM], held[NBK][AM];
-#pragma unroll
-    for (int bm = 0; bm < AM; ++bm)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-            acc[bm][e] = 0.0f;
-
-    const int npre = min(NSTAGE, ntiles);
-    for (int g = 0; g < npre; ++g)
-        issue(g * STAGE, g);
-
-    int rd = 0;
-    for (int g = 0; g < ntiles; ++g) {
-        wait_tiles(min(NSTAGE - 1, ntiles - 1 - g));   // tile g is in this wave's LDS
-#pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-            const bf16x8_t af = *(const bf16x8_t *)(smem + ((a_addr + rd) ^ (32 * s)));
-            bf16x8_t bf[AM];
-#pragma unroll
-            for (int bm = 0; bm < AM; ++bm)
-                bf[bm] = *(const bf16x8_t *)(smem + ((b_addr + rd + bm * 32 * ROW_BYTES) ^ (32 * s)));
-#pragma unroll
-            for (int bm = 0; bm < AM; ++bm)
-                acc[bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[bm], acc[bm], 0, 0, 0);
-        }
-        if (g + NSTAGE < ntiles) {
-            wait_vmcnt<63>();   // lgkmcnt(0): this wave's reads of the stage are complete
-            issue(rd, g + NSTAGE);
-        }
-        rd = (rd + STAGE == WAVE_LDS) ? 0 : rd + STAGE;
-
-        const int blk = g / nk;
-        if (g - blk * nk == nk - 1)
-            lowm::lowm_block_done<AM, NBK, OUT_BF16>(held, acc, blk, nblocks, v_lo, v_hi, rows, fr, hi, out, ldo);
-    }
-}
 
 // At most n (0 <= n <= MAXN) DMA tiles of T instructions each still in flight.
 template <int T, int MAXN>
@@ -1510,11 +1389,14 @@ __device__ __forceinline__ void wait_tiles_upto(int n)
     }
 }
 
-// Low-M gather-GEMM with the H tile shared by the workgroup (M <= 32 * AM).
+// Low-M gather-GEMM (M <= 32 * AM): the work is streaming W once from HBM, with the H
+// tile shared by the workgroup.
 //
-// The W stream is as in gather_gemm_lowm_kernel: wave w of the grid owns an equal,
-// contiguous range of vocabulary rows and walks it in 32-row blocks, each a full K loop,
-// through a private LDS ring.  Here every wave of the grid runs the same number of
+// Wave w of the grid owns an equal, contiguous range of vocabulary rows (so every wave
+// streams the same number of W bytes) and walks it in 32-row blocks (one MFMA A block),
+// each a full K loop, through a private LDS ring filled by its own global_load_lds DMA;
+// the ring keeps running across blocks.  The masked rows (at most 32 * AM) are the MFMA B
+// operand.  Every wave of the grid runs the same number of
 // (block, K tile) steps (waves whose range is short run padding blocks of clamped rows
 // that are never stored), so the four waves of a workgroup need the same H tile at the
 // same step.  That tile (32 * AM masked rows x 64 k) is fetched once per workgroup into a
@@ -1523,7 +1405,9 @@ __device__ __forceinline__ void wait_tiles_upto(int n)
 // LDS to a deeper W ring (8 stages for AM = 1: seven 4 KiB W tiles in flight per wave
 // while one is consumed).  The barrier also tells each wave that every other wave has
 // finished reading the previous step's slot, which is then refilled.
-// Same MFMA, operand roles and k order as the tiled kernel: results are bit-identical.
+// (Against a per-wave copy of H, measured earlier as its own variant, this reads H from L2
+// four times less.)  Same MFMA, operand roles and k order as the tiled kernel: results
+// are bit-identical.
 template <int AM, int NSTAGE, bool OUT_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
 gather_gemm_lowm_shared_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict__ idx, int32_t rows,
@@ -1816,25 +1700,6 @@ hipError_t launch_defer(const void *H, const int32_t *idx, int64_t rows, const v
 }
 
 template <int AM>
-hipError_t launch_lowm(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V, int64_t d,
-                       void *out, int64_t ldo, bool out_bf16, hipStream_t stream)
-{
-    constexpr int NSTAGE = AM == 1 ? 5 : 3;   // 40 KiB of LDS per wave
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    // one workgroup (four streams) per CU, but never fewer than 32 rows per stream
-    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cus, (V + 127) / 128));
-    if (out_bf16)
-        hipLaunchKernelGGL((gather_gemm_lowm_kernel<AM, NSTAGE, true>), dim3(grid), dim3(256), 0, stream,
-                           (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d, out, ldo);
-    else
-        hipLaunchKernelGGL((gather_gemm_lowm_kernel<AM, NSTAGE, false>), dim3(grid), dim3(256), 0, stream,
-                           (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d, out, ldo);
-    return hipGetLastError();
-}
-
-template <int AM>
 hipError_t launch_lowm_shared(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V, int64_t d,
                               void *out, int64_t ldo, bool out_bf16, hipStream_t stream)
 {
@@ -1861,25 +1726,11 @@ bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V)
     case kVariantF32:
     case kVariantBf16Simple:
         return (rows + 63) / 64 <= 0x7fffffffLL && (V + 63) / 64 <= 65535;
-    case kVariantBf16Tile256:
-    case kVariantBf16K32S3:
-    case kVariantBf16K32S4:
-    case kVariantBf16K32S5:
-    case kVariantBf16K64Spread2:
-    case kVariantBf16K64Spread4:
-    case kVariantBf16PersistK64:
-    case kVariantBf16PersistK64S4:
-    case kVariantBf16PersistK32:
     case kVariantBf16W8K64S2:
-    case kVariantBf16W8K64:
-    case kVariantBf16W8K32S4:
-    case kVariantBf16DeferS8:
+    case kVariantBf16PersistK32:
     case kVariantBf16DeferS4I8:
-    case kVariantBf16DeferS16:
-    case kVariantBf16M16:
     case kVariantBf16M16S1:
         return ((rows + 255) / 256) * ((V + 255) / 256) <= 0x7fffffffLL;
-    case kVariantBf16LowM:
     case kVariantBf16LowMShared:
         return rows <= 64;
     default:
@@ -1935,46 +1786,15 @@ hipError_t launch_gather_gemm(int variant, const void *H, const int32_t *idx, in
                                idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V, (int32_t)d, out, ldo);
         return hipGetLastError();
     }
-    case kVariantBf16Tile256:
-        return launch_bf16<256, 256, 64, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
-    case kVariantBf16K32S3:
-        return launch_bf16<256, 256, 32, 3, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
-    case kVariantBf16K32S4:
-        return launch_bf16<256, 256, 32, 4, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
-    case kVariantBf16K32S5:
-        return launch_bf16<256, 256, 32, 5, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
-    case kVariantBf16K64Spread2:
-        return launch_bf16<256, 256, 64, 2, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
-    case kVariantBf16K64Spread4:
-        return launch_bf16<256, 256, 64, 2, 4>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
     case kVariantBf16W8K64S2:
         return launch_bf16<256, 256, 64, 2, 2, 8>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
-    case kVariantBf16W8K64:
-        return launch_bf16<256, 256, 64, 2, 1, 8>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
-    case kVariantBf16W8K32S4:
-        return launch_bf16<256, 256, 32, 4, 2, 8>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
-    case kVariantBf16DeferS8:
-        return out_bf16 ? launch_defer<2, 8, 0>(H, idx, rows, W, V, d, out, ldo, group_m, stream) : hipErrorInvalidValue;
     case kVariantBf16DeferS4I8:
         return out_bf16 ? launch_defer<2, 4, 8>(H, idx, rows, W, V, d, out, ldo, group_m, stream) : hipErrorInvalidValue;
-    case kVariantBf16DeferS16:
-        return out_bf16 ? launch_defer<2, 16, 0>(H, idx, rows, W, V, d, out, ldo, group_m, stream) : hipErrorInvalidValue;
-    case kVariantBf16M16:
-        return out_bf16 ? launch_defer<2, 1, 16, true, false, true>(H, idx, rows, W, V, d, out, ldo, group_m, stream)
-                        : hipErrorInvalidValue;
     case kVariantBf16M16S1:
         return out_bf16 ? launch_defer<1, 1, 16, true, false, true>(H, idx, rows, W, V, d, out, ldo, group_m, stream)
                         : hipErrorInvalidValue;
-    case kVariantBf16PersistK64:
-        return launch_persist<64, 2, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
-    case kVariantBf16PersistK64S4:
-        return launch_persist<64, 2, 4>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
     case kVariantBf16PersistK32:
         return launch_persist<32, 4, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);
-    case kVariantBf16LowM:
-        if (rows <= 32)
-            return launch_lowm<1>(H, idx, rows, W, V, d, out, ldo, out_bf16, stream);
-        return launch_lowm<2>(H, idx, rows, W, V, d, out, ldo, out_bf16, stream);
     case kVariantBf16LowMShared:
         if (rows <= 32)
             return launch_lowm_shared<1>(H, idx, rows, W, V, d, out, ldo, out_bf16, stream);

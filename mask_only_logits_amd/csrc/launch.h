@@ -16,30 +16,18 @@ hipError_t launch_mask_compact_batched(const int32_t *tokens, int64_t L, const i
                                        int32_t nseq, int32_t mask_id, int32_t *idx,
                                        int32_t *idx_offsets, hipStream_t stream);
 
-// Kernel variants of the logits GEMM.
+// Kernel variants of the logits GEMM.  The numbers are stable identifiers (reported by
+// mosaic_logits_variant and accepted by MOSAIC_TUNE); gaps are retired experiment forms.
 enum LogitsVariant : int {
-    kVariantF32 = 0,          // fp32 inputs: LDS-tiled FMA kernel
-    kVariantBf16Tile256 = 1,  // bf16 inputs, d % 64 == 0: 256 x 256 MFMA tile, 2-stage LDS pipeline
-    kVariantBf16Simple = 2,   // bf16 inputs, any d % 8 == 0: LDS-tiled FMA kernel
-    kVariantBf16K32S3 = 3,    // bf16, d % 32 == 0: 256 x 256 tile, K 32 deep, 3 LDS stages (DMA over 2 sub-steps)
-    kVariantBf16K32S4 = 4,    // ... 4 LDS stages
-    kVariantBf16K32S5 = 5,    // ... 5 LDS stages (160 KiB)
-    kVariantBf16LowM = 6,     // bf16, d % 64 == 0, M <= 64: W-streaming persistent kernel
-    kVariantBf16K64Spread2 = 7,  // as 1, refill DMA spread over 2 k sub-steps
-    kVariantBf16K64Spread4 = 8,  // as 1, refill DMA spread over 4 k sub-steps
-    kVariantBf16PersistK64 = 9,    // persistent 256 x 256, BK 64, 2 stages, DMA over 2 sub-steps
-    kVariantBf16PersistK64S4 = 10, // ... DMA over 4 sub-steps
-    kVariantBf16PersistK32 = 11,   // persistent 256 x 256, BK 32, 4 stages
-    kVariantBf16W8K64S2 = 12,      // 256 x 256, 8 waves (2 per SIMD), BK 64, DMA over 2 sub-steps
-    kVariantBf16W8K64 = 13,        // ... refill DMA in one sub-step
-    kVariantBf16W8K32S4 = 14,      // 256 x 256, 8 waves, BK 32, 4 stages
-    kVariantBf16DeferS8 = 15,      // persistent 8-wave, bf16 out, tile stores spread over 8 K steps
-    kVariantBf16DeferS4I8 = 16,    // ... half the stores at once, half over 4 K steps
-    kVariantBf16DeferS16 = 17,     // ... stores spread over 16 K steps
-    kVariantBf16M16 = 18,          // persistent 8-wave, 16 x 16 x 32 MFMA, bf16 out, stores at each tile's end
-    kVariantBf16M16S1 = 19,        // ... refill DMA in one k sub-step (the bf16-output default)
+    kVariantF32 = 0,               // fp32 inputs: LDS-tiled FMA kernel
+    kVariantBf16Simple = 2,        // bf16 inputs, any d % 8 == 0: LDS-tiled FMA kernel
+    kVariantBf16PersistK32 = 11,   // bf16, d % 32 == 0: persistent 256 x 256, 4 waves, BK 32, 4 stages
+    kVariantBf16W8K64S2 = 12,      // bf16, d % 64 == 0: 256 x 256, 8 waves, BK 64 (the bf16 -> fp32 default)
+    kVariantBf16DeferS4I8 = 16,    // bf16 -> bf16, d % 64 == 0: persistent 8-wave, 32 x 32 x 16 MFMA,
+                                   // half the stores deferred over 4 K steps (comparison form)
+    kVariantBf16M16S1 = 19,        // bf16 -> bf16, d % 64 == 0: persistent 8-wave, 16 x 16 x 32 MFMA
+                                   // (the bf16-output default)
     kVariantBf16LowMShared = 20,   // bf16, d % 64 == 0, M <= 64: W streaming with a workgroup-shared H tile
-    kNumVariants = 21,
 };
 
 // Default number of row tiles that share the W slabs of one XCD (tile order).

@@ -27,6 +27,9 @@ constexpr int64_t kMaxPos = 0x7fffffffLL;   // positions and rows are int32
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// ceil(a / b) for a >= 0, b > 0, without the overflow of (a + b - 1) / b near INT64_MAX.
+int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
+
 int64_t esize_of(mosaic_dtype_t t) { return t == MOSAIC_F32 ? 4 : (t == MOSAIC_BF16 ? 2 : 0); }
 
 // M * V * esize without int64 overflow; -1 on overflow.
@@ -134,24 +137,10 @@ bool variant_can_run(int v, int64_t M, int64_t d, mosaic_dtype_t in, mosaic_dtyp
     switch (v) {
     case mosaic::kVariantF32: return in == MOSAIC_F32 && out == MOSAIC_F32 && d % 4 == 0;
     case mosaic::kVariantBf16Simple: return bf16_in && d % 8 == 0;
-    case mosaic::kVariantBf16Tile256:
-    case mosaic::kVariantBf16K64Spread2:
-    case mosaic::kVariantBf16K64Spread4:
-    case mosaic::kVariantBf16PersistK64:
-    case mosaic::kVariantBf16PersistK64S4:
-    case mosaic::kVariantBf16W8K64S2:
-    case mosaic::kVariantBf16W8K64: return bf16_in && d % 64 == 0 && small_d;
-    case mosaic::kVariantBf16DeferS8:
+    case mosaic::kVariantBf16W8K64S2: return bf16_in && d % 64 == 0 && small_d;
     case mosaic::kVariantBf16DeferS4I8:
-    case mosaic::kVariantBf16DeferS16:
-    case mosaic::kVariantBf16M16:
     case mosaic::kVariantBf16M16S1: return in == MOSAIC_BF16 && out == MOSAIC_BF16 && d % 64 == 0 && small_d;
-    case mosaic::kVariantBf16W8K32S4:
     case mosaic::kVariantBf16PersistK32: return bf16_in && d % 32 == 0 && small_d;
-    case mosaic::kVariantBf16K32S3:
-    case mosaic::kVariantBf16K32S4:
-    case mosaic::kVariantBf16K32S5: return bf16_in && d % 32 == 0 && small_d;
-    case mosaic::kVariantBf16LowM:
     case mosaic::kVariantBf16LowMShared: return bf16_in && d % 64 == 0 && small_d && M <= 64;
     default: return false;
     }
@@ -235,7 +224,7 @@ int64_t mosaic_num_chunks(int64_t M, int64_t chunk_rows)
         return 0;
     if (chunk_rows <= 0 || chunk_rows >= M)
         return 1;
-    return (M + chunk_rows - 1) / chunk_rows;
+    return ceil_div(M, chunk_rows);
 }
 
 mosaic_status_t mosaic_logits_bytes(int64_t rows, int64_t V, mosaic_dtype_t dt, int64_t *bytes)
@@ -337,7 +326,7 @@ mosaic_status_t mosaic_masked_logits(const void *H, int64_t L, int64_t d, const 
         return MOSAIC_ERR_UNSUPPORTED;
     const int v_full = pick_variant(C, V, d, in_dtype, out_dtype);
     int v_tail = pick_variant(tail, V, d, in_dtype, out_dtype);
-    if (v_tail != mosaic::kVariantBf16LowM && v_tail != mosaic::kVariantBf16LowMShared)
+    if (v_tail != mosaic::kVariantBf16LowMShared)
         v_tail = v_full;
     if (v_full < 0 || v_tail < 0 || !mosaic::gather_gemm_grid_fits(v_full, C, V) ||
         !mosaic::gather_gemm_grid_fits(v_tail, tail, V))
@@ -382,8 +371,8 @@ mosaic_status_t mosaic_lazy_chunk_rows(int64_t M, int64_t V, mosaic_dtype_t out_
     const int64_t r = budget_bytes / es / V;
     if (r < 1)
         return MOSAIC_ERR_UNSUPPORTED;
-    const int64_t k = (M + r - 1) / r;
-    *chunk_rows = (M + k - 1) / k;
+    const int64_t k = ceil_div(M, r);
+    *chunk_rows = ceil_div(M, k);
     *num_chunks = k;
     return MOSAIC_OK;
 }
@@ -399,7 +388,7 @@ static int64_t argmax_lse_partials_bytes(int64_t rows, int64_t V)
 {
     if (rows < 0 || V < 0)
         return -1;
-    const int64_t ncol = (V + 255) / 256;
+    const int64_t ncol = ceil_div(V, 256);
     const int64_t n = checked_bytes(ncol, rows, 12);
     return n < 0 ? -1 : n;
 }
@@ -461,7 +450,7 @@ static mosaic_status_t argmax_lse_impl(const void *H, int64_t L, int64_t d, cons
     // workspace: pmax, parg, psum, each [ceil(V/256)][C] 4-byte words; every entry is written
     // by a chunk's GEMM launch before that chunk's finish kernel reads it, so nothing needs
     // clearing
-    const int64_t plane = (V + 255) / 256 * C;
+    const int64_t plane = ceil_div(V, 256) * C;
     float *pmax = (float *)workspace;
     int32_t *parg = (int32_t *)(pmax + plane);
     float *psum = (float *)(parg + plane);
@@ -536,7 +525,9 @@ static int64_t fp8_chunk_bytes(int64_t rows, int64_t d)
     const int64_t codes = checked_bytes(rows, d, 1);
     if (codes < 0 || rows < 0)
         return -1;
-    const int64_t aligned = (codes + 15) / 16 * 16;
+    if (codes > INT64_MAX - 15)
+        return -1;
+    const int64_t aligned = ceil_div(codes, 16) * 16;
     if (aligned > INT64_MAX - 4 * rows)
         return -1;
     return aligned + 4 * rows;

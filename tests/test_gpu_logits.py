@@ -78,10 +78,10 @@ LOWM_CASES = [
 ]
 
 
-@pytest.mark.parametrize("variant", [6, 20])
+@pytest.mark.parametrize("variant", [20])
 @pytest.mark.parametrize("dt_out,L,d,V,M", LOWM_CASES)
 def test_parity_lowm(m, lib_env, variant, dt_out, L, d, V, M):
-    # both low-M streaming kernels: private H copies per wave (6) and a workgroup-shared H tile (20)
+    # the low-M streaming kernel (W streamed once, a workgroup-shared H tile)
     lib_env("MOSAIC_TUNE", f"variant={variant}")
     assert m.mosaic_logits_variant(M, V, d, torch.bfloat16, TD[dt_out]) == variant
     wl = inputs.make_random(L + d + V + M, L=L, d=d, V=V, M=M, dtype="bf16")
@@ -89,6 +89,11 @@ def test_parity_lowm(m, lib_env, variant, dt_out, L, d, V, M):
     out = m.mosaic_masked_logits(wl.H.to(DEV), idx_d, wl.W.to(DEV), out_dtype=TD[dt_out])
     torch.cuda.synchronize()
     assert_close(out, oracle.masked_logits(wl.H, idx, wl.W), f"lowm {d},{V},{M}")
+
+
+# every bf16 MFMA kernel form the library can select: persistent BK-32 (11), 8-wave tiled
+# (12), persistent 32 x 32 x 16 (16), persistent 16 x 16 x 32 (19), low-M streaming (20)
+BF16_MFMA_VARIANTS = (11, 12, 16, 19, 20)
 
 
 @pytest.mark.parametrize("M,d,V,out", [(20, 3584, 5000, "bf16"), (64, 256, 1001, "f32"), (700, 512, 1000, "bf16"),
@@ -105,13 +110,11 @@ def test_bf16_variants_bit_identical(m, lib_env, M, d, V, out):
     _, idx_d = _gpu_idx(wl)
     H, W = wl.H.to(DEV), wl.W.to(DEV)
     ref = m.mosaic_masked_logits(H, idx_d, W, out_dtype=TD[out])
-    for v in range(1, 21):
-        if v == 2:
-            continue
-        if v in (6, 20) and M > 64:
+    for v in BF16_MFMA_VARIANTS:
+        if v == 20 and M > 64:
             continue
         lib_env("MOSAIC_TUNE", f"variant={v}")
-        if out == "bf16" or v < 15:            # the deferred-store kernels write bf16 only
+        if out == "bf16" or v not in (16, 19):  # the persistent deferred-store kernels write bf16 only
             assert m.mosaic_logits_variant(M, V, d, torch.bfloat16, TD[out]) == v
         got = m.mosaic_masked_logits(H, idx_d, W, out_dtype=TD[out])
         torch.cuda.synchronize()
