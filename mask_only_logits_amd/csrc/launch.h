@@ -25,9 +25,11 @@ enum LogitsVariant : int {
     kVariantBf16W8K64S2 = 12,      // bf16, d % 64 == 0: 256 x 256, 8 waves, BK 64 (the bf16 -> fp32 default)
     kVariantBf16DeferS4I8 = 16,    // bf16 -> bf16, d % 64 == 0: persistent 8-wave, 32 x 32 x 16 MFMA,
                                    // half the stores deferred over 4 K steps (comparison form)
-    kVariantBf16M16S1 = 19,        // bf16 -> bf16, d % 64 == 0: persistent 8-wave, 16 x 16 x 32 MFMA
-                                   // (the bf16-output default)
+    kVariantBf16M16S1 = 19,        // bf16 -> bf16, d % 64 == 0: persistent 8-wave, 16 x 16 x 32 MFMA,
+                                   // every wave requests K tiles
     kVariantBf16LowMShared = 20,   // bf16, d % 64 == 0, M <= 64: W streaming with a workgroup-shared H tile
+    kVariantBf16M16Dma4 = 21,      // bf16 -> bf16, d % 64 == 0: as 19, K tiles requested by one wave per
+                                   // SIMD (the bf16-output default)
 };
 
 // Default number of row tiles that share the W slabs of one XCD (tile order).

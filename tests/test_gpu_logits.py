@@ -92,8 +92,9 @@ def test_parity_lowm(m, lib_env, variant, dt_out, L, d, V, M):
 
 
 # every bf16 MFMA kernel form the library can select: persistent BK-32 (11), 8-wave tiled
-# (12), persistent 32 x 32 x 16 (16), persistent 16 x 16 x 32 (19), low-M streaming (20)
-BF16_MFMA_VARIANTS = (11, 12, 16, 19, 20)
+# (12), persistent 32 x 32 x 16 (16), persistent 16 x 16 x 32 with every wave requesting K
+# tiles (19) or one wave per SIMD (21), low-M streaming (20)
+BF16_MFMA_VARIANTS = (11, 12, 16, 19, 20, 21)
 
 
 @pytest.mark.parametrize("M,d,V,out", [(20, 3584, 5000, "bf16"), (64, 256, 1001, "f32"), (700, 512, 1000, "bf16"),
@@ -114,7 +115,7 @@ def test_bf16_variants_bit_identical(m, lib_env, M, d, V, out):
         if v == 20 and M > 64:
             continue
         lib_env("MOSAIC_TUNE", f"variant={v}")
-        if out == "bf16" or v not in (16, 19):  # the persistent deferred-store kernels write bf16 only
+        if out == "bf16" or v not in (16, 19, 21):  # the persistent deferred-store kernels write bf16 only
             assert m.mosaic_logits_variant(M, V, d, torch.bfloat16, TD[out]) == v
         got = m.mosaic_masked_logits(H, idx_d, W, out_dtype=TD[out])
         torch.cuda.synchronize()
