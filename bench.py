@@ -444,7 +444,7 @@ def main():
         "gather_gemm_bf16_defer_kernel" if consumer else {
             0: "gather_gemm_f32_kernel", 2: "gather_gemm_bf16_simple_kernel", 11: "gather_gemm_bf16_persist_kernel",
             12: "gather_gemm_bf16_kernel", 16: "gather_gemm_bf16_defer_kernel", 19: "gather_gemm_bf16_defer_kernel",
-            21: "gather_gemm_bf16_defer_kernel",
+            21: "gather_gemm_bf16_defer_kernel", 22: "gather_gemm_bf16_defer_kernel",
             20: "gather_gemm_lowm_shared_kernel"}.get(variant, "gather_gemm")
     if variant in LOWM_VARIANTS or fp8_lowm:
         # streaming W is the bound: algorithmic bytes per launch over the launch time

@@ -711,7 +711,7 @@ gather_gemm_bf16_persist_kernel(const __bf16 *__restrict__ H, const int32_t *__r
 //  * 256 x 256 tiles, K staged 64 deep in two LDS stages, eight waves: two per SIMD, so
 //    while one wave waits (DMA issue, barrier) the other keeps the matrix core busy.  A
 //    wave owns 128 vocabulary x 64 masked rows (4 x 2 MFMA blocks, 128 accumulators).
-//  * Tile list per XCD as in the persistent kernel above.
+//  * Tile lists per XCD, with the XCDs side by side on large launches (below).
 //  * When a tile's K loop ends, its results are rounded to bf16 and arranged for 16-byte
 //    stores (permlane32_swap) in registers; NIMM of its stores go out at once and the rest
 //    are issued over the first DEFER K steps of the next tile.  Every workgroup reaches a
@@ -740,15 +740,23 @@ gather_gemm_bf16_persist_kernel(const __bf16 *__restrict__ H, const int32_t *__r
 // combine their consumer partials through permlane16_swap and permlane32_swap.
 //
 // DMAW: the waves that request K tiles.  8: every wave requests its eighth of each K tile.
-// 4 (the 16 x 16 x 32 default): only waves 0-3, one per SIMD, request K tiles, a quarter
-// each, and waves 4-7 issue no DMA at all.  A DMA request blocks its wave's instruction
-// stream while the texture path is busy (about 100 cycles per request here); with every
-// wave requesting, both waves of a SIMD stall on the same requests at the start of a K
-// step and its matrix core idles, while with one requesting wave per SIMD the other keeps
-// issuing MFMAs.  The two kinds of wave run separate instantiations of the K loop (no
-// per-request branch).  Measured +4% on the headline (1381-1401 against 1325-1347
-// TFLOP/s, interleaved on one box each), bit-identical.
-template <int NSPREAD, int DEFER, int NIMM, bool STORE = true, bool REDUCE = false, bool M16 = false, int DMAW = 8>
+// 4 (the 16 x 16 x 32 defaults): only waves 0-3, one per SIMD, request K tiles, a quarter
+// each, and waves 4-7 issue no DMA at all, so one wave of each SIMD never waits on the
+// texture path and keeps its matrix core fed while the other issues requests.  The two
+// kinds of wave run separate instantiations of the K loop (no per-request branch).
+// Measured on 4096 rows x 4096 x 126464: moving one launch's K tiles alone takes 1.76 ms
+// with 4 requesting waves and 1.94 ms with 8; the GEMM runs 3-5% faster; bit-identical.
+//
+// DEEP: 0: two LDS stages per operand, so the refill issued at step kt's barrier must land
+// by the next one (a single batch of requests in flight, and the texture path idles between
+// batches).  1: W gets a third stage (160 KiB of LDS in all) and runs a step further ahead,
+// so a second batch is in flight while a step's H rows land: 3-7% faster (4096 x 4096 x
+// 126464: 1448-1452 against 1393-1395 TFLOP/s).  (With the XCDs out of step on large
+// launches it was 5-6% slower there; with the tile order below it is not.)  2 (H
+// three-deep instead) gained nothing.  REDUCE needs LDS beyond the five stages, so the
+// per-row consumer keeps two.
+template <int NSPREAD, int DEFER, int NIMM, bool STORE = true, bool REDUCE = false, bool M16 = false, int DMAW = 8,
+          int DEEP = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
 gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict__ idx, int32_t rows,
                               const __bf16 *__restrict__ W, int32_t V, int32_t d, __bf16 *__restrict__ out,
@@ -756,6 +764,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
                               int32_t *__restrict__ parg, float *__restrict__ psum)
 {
     constexpr int NW = 8, BV = 256, BM = 256, BK = 64, NSTAGE = 2;
+    constexpr int WST = DEEP == 1 ? 3 : 2, HST = DEEP == 2 ? 3 : 2;   // W and H stages
     constexpr int ROW_BYTES = BK * 2;
     constexpr int CHUNKS = BK / 8;
     constexpr int RPI = 64 / CHUNKS;
@@ -764,13 +773,14 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     // LDS: the two W stages (32 KiB each), then the two H stages; a refill requests H's
     // rows before W's.  Against alternating W and H stages with W first, measured on one
     // box: +0.5-1% for the 16 x 16 x 32 form, -2% for the 32 x 32 x 16 form.
-    constexpr int H_BASE = NSTAGE * W_TILE;
+    constexpr int H_BASE = WST * W_TILE;
     constexpr int WV = BV / 2, WM = BM / (NW / 2);
     constexpr int MB = M16 ? 16 : 32;         // MFMA block edge
     constexpr int KI = M16 ? 32 : 16;         // k per MFMA
     constexpr int NACC = MB * MB / 64;        // accumulators per lane and block
     constexpr int AV = WV / MB, AM = WM / MB;
     constexpr int LW = BV / RPI / DMAW, LH = BM / RPI / DMAW;   // DMA instructions of a DMA wave
+    constexpr int L3 = DEEP == 1 ? LW : DEEP == 2 ? LH : 0;    // those of the operand with a third stage
     constexpr int NSUB = BK / KI;
     constexpr int NDMA = LW + LH;
     constexpr int NFR = AV + AM;
@@ -788,9 +798,10 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     // can no longer tell the stage DMA from the fragment reads and waits for every DMA
     // before each read (measured 17% slower).
     constexpr int RED_BYTES = REDUCE ? 3 * BM * 4 : 0;
-    static_assert(H_BASE + NSTAGE * H_TILE + RED_BYTES <= 160 * 1024, "LDS");
-    __shared__ __attribute__((aligned(1024))) char smem[H_BASE + NSTAGE * H_TILE + RED_BYTES];
-    float *const red_lds = (float *)(smem + H_BASE + NSTAGE * H_TILE);
+    static_assert(H_BASE + HST * H_TILE + RED_BYTES <= 160 * 1024, "LDS");
+    static_assert(DEEP == 0 || (NSPREAD == 1 && M16 && NIMM == NST), "a third stage: 16 x 16 form, no deferral");
+    __shared__ __attribute__((aligned(1024))) char smem[H_BASE + HST * H_TILE + RED_BYTES];
+    float *const red_lds = (float *)(smem + H_BASE + HST * H_TILE);
 
     const int nvt = (V + BV - 1) / BV;
     const int nmt = (rows + BM - 1) / BM;
@@ -801,17 +812,36 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     const int G = gridDim.x;                    // a multiple of 8
     const int per_xcd = G >> 3;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int q = ntiles >> 3, rem = ntiles & 7;
+    const int per_group = group_m * nvt;
+    // The row tiles come in super-groups of 8 * group_m.  In a full one, XCD x takes row
+    // tiles x, x + 8, ... and every vocabulary tile of them in order, so the eight XCDs sweep
+    // the vocabulary side by side and read each W slab at about the same time (from HBM
+    // once, then from the Infinity Cache).  The tiles of the rows after the last full
+    // super-group go to the XCDs in eight contiguous runs of group order (group_m row tiles
+    // by every vocabulary tile): XCD x takes the x-th run.  With the XCDs out of step (the
+    // runs alone, on 84 and 116 row tiles) the GEMM measured 2-4% slower.
+    const int sg = 8 * group_m;
+    const int nfull = nmt / sg;
+    const int full_tiles = nfull * per_group;  // per XCD
+    const int rtiles = ntiles - 8 * full_tiles;
+    const int q = rtiles >> 3, rem = rtiles & 7;
     const int start = xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q;
-    const int count = q + (xcd < rem ? 1 : 0);
+    const int count = full_tiles + q + (xcd < rem ? 1 : 0);
     const int n_my = slot < count ? (count - slot + per_xcd - 1) / per_xcd : 0;
     if (n_my == 0)
         return;
-    auto tile_coords = [&](int i, int &m0, int &v0) {
-        const int t = start + slot + i * per_xcd;
-        const int per_group = group_m * nvt;
+    auto tile_coords = [&](int i, int &m0, int &v0) __attribute__((always_inline)) {
+        const int tx = slot + i * per_xcd;
+        if (tx < full_tiles) {
+            const int s = tx / per_group;
+            const int t = 8 * (tx - s * per_group) + xcd;
+            m0 = (s * sg + t % sg) * BM;
+            v0 = (t / sg) * BV;
+            return;
+        }
+        const int t = start + tx - full_tiles;
         const int g = t / per_group;
-        const int first_m = g * group_m;
+        const int first_m = nfull * sg + g * group_m;
         const int gsz = min(nmt - first_m, group_m);
         const int local = t - g * per_group;
         m0 = (first_m + local % gsz) * BM;
@@ -830,7 +860,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     auto row_h = [&](int j) { return (dwave * LH + j) * RPI + lane / CHUNKS; };
     auto chunk_of = [&](int r) { return ((lane % CHUNKS) ^ swz<BK>(r)) * 16; };
     int32_t hidx_nxt[LH];                       // H row ids of the next tile (loaded a tile ahead)
-    auto load_hidx = [&](int i) {
+    auto load_hidx = [&](int i) __attribute__((always_inline)) {
         if (i >= n_my)
             return;
         int m0, v0;
@@ -842,7 +872,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     const char *wbase;
     uint32_t woff[LW];
     const char *hsrc[LH];
-    auto make_src = [&](int i) {
+    auto make_src = [&](int i) __attribute__((always_inline)) {
         int m0, v0;
         tile_coords(i, m0, v0);
         wbase = (const char *)(W + (int64_t)v0 * d);
@@ -861,7 +891,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
 
     // Part p of the refill with K tile kt: H's rows into the H stage at byte offset rh, then
     // W's into the W stage at rw.
-    auto issue_part = [&](int rw, int rh, int kt, int p) {
+    auto issue_part = [&](int rw, int rh, int kt, int p) __attribute__((always_inline)) {
         const int kb = kt * ROW_BYTES;
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) {
@@ -876,11 +906,26 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
                                                  0);
         }
     };
-    auto next_w = [](int rw) { return rw + W_TILE == NSTAGE * W_TILE ? 0 : rw + W_TILE; };
-    auto next_h = [](int rh) { return rh + H_TILE == H_BASE + NSTAGE * H_TILE ? H_BASE : rh + H_TILE; };
+    auto next_w = [](int rw) { return rw + W_TILE == WST * W_TILE ? 0 : rw + W_TILE; };
+    auto next_h = [](int rh) { return rh + H_TILE == H_BASE + HST * H_TILE ? H_BASE : rh + H_TILE; };
+    // One operand's rows of K tile kt (the 16 x 16 forms with a third stage)
+    auto issue_h = [&](int rh, int kt) __attribute__((always_inline)) {
+        const int kb = kt * ROW_BYTES;
+#pragma unroll
+        for (int i = 0; i < LH; ++i)
+            __builtin_amdgcn_global_load_lds((const void *)(hsrc[i] + kb),
+                                             (lds_void_t *)(smem + rh + (dwave * LH + i) * 1024), 16, 0, 0);
+    };
+    auto issue_w = [&](int rw, int kt) __attribute__((always_inline)) {
+        const int kb = kt * ROW_BYTES;
+#pragma unroll
+        for (int i = 0; i < LW; ++i)
+            __builtin_amdgcn_global_load_lds((const void *)(wbase + kb + woff[i]),
+                                             (lds_void_t *)(smem + rw + (dwave * LW + i) * 1024), 16, 0, 0);
+    };
 
     acc_t acc[AV][AM];
-    auto zero_acc = [&]() {
+    auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int a = 0; a < AV; ++a)
 #pragma unroll
@@ -1002,7 +1047,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     uint32_t pk[NST][4];
     int pm0 = 0, pv0 = 0;
     const bool vec_ok = ((uintptr_t)out & 15) == 0 && (ldo & 7) == 0;
-    auto store_one = [&](int j) {
+    auto store_one = [&](int j) __attribute__((always_inline)) {
         int row, v;
         if constexpr (M16) {
             const int ap = j / AM, bm = j % AM;
@@ -1029,7 +1074,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     // lanes 32-63 entries 8-15 / 24-31; 16 x 16: permlane16_swap trades the odd-qd lanes'
     // words of the first block of a pair for the even-qd lanes' words of the second), then
     // restart the accumulators
-    auto pack = [&]() {
+    auto pack = [&]() __attribute__((always_inline)) {
         if constexpr (M16) {
 #pragma unroll
             for (int ap = 0; ap < AV / 2; ++ap)
@@ -1077,7 +1122,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     // keep the smaller index, sums are rescaled to the new max.  An empty partial is
     // (-inf, INT32_MAX, 0).
     constexpr float kLog2e = 1.4426950408889634f;
-    auto combine = [&](float &m, int &a, float &sm, float m2, int a2, float s2) {
+    auto combine = [&](float &m, int &a, float &sm, float m2, int a2, float s2) __attribute__((always_inline)) {
         const float mm = fmaxf(m, m2);
         const bool take = m2 > m || (m2 == m && a2 < a);
         const float e1 = (m == -INFINITY) ? 0.0f : sm * __builtin_amdgcn_exp2f((m - mm) * kLog2e);
@@ -1094,7 +1139,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     // half's waves leave theirs in LDS.
     const int row_lane = M16 ? r16 : fr;
     const bool row_owner = M16 ? qd == 0 : hi == 0;
-    auto reduce_part1 = [&](int v0) {
+    auto reduce_part1 = [&](int v0) __attribute__((always_inline)) {
 #pragma unroll
         for (int bm = 0; bm < AM; ++bm) {
             float m = -INFINITY, sm = 0.0f;
@@ -1154,7 +1199,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
         }
     };
     // after a barrier: the lower half's waves add the upper half and write the partial
-    auto reduce_part2 = [&](int m0, int v0) {
+    auto reduce_part2 = [&](int m0, int v0) __attribute__((always_inline)) {
         if (wv != 0 || !row_owner)
             return;
         const int64_t col = (int64_t)(v0 / BV) * rows;
@@ -1174,16 +1219,23 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
 
     bf16x8_t af[2][AV], bf[2][AM];
     // A tile's first two K tiles, in the order the waits count on: H0, W0, H1, W1
-    auto prologue = [&]() {
+    auto prologue = [&]() __attribute__((always_inline)) {
         for (int s = 0; s < min(NSTAGE, nk); ++s)
 #pragma unroll
             for (int p = 0; p < NSPREAD; ++p)
                 issue_part(s * W_TILE, H_BASE + s * H_TILE, s, p);
+        if constexpr (DEEP == 1) {
+            if (nk > 2)
+                issue_w(2 * W_TILE, 2);
+        } else if constexpr (DEEP == 2) {
+            if (nk > 2)
+                issue_h(H_BASE + 2 * H_TILE, 2);
+        }
     };
     if (dma_wave)
         prologue();
 
-    auto main_loop = [&](auto dma_tag) {
+    auto main_loop = [&](auto dma_tag) __attribute__((always_inline)) {
     constexpr bool DMA_ON = decltype(dma_tag)::value;
     auto issue_part_t = [&](int rw, int rh, int kt, int p) {
         if constexpr (DMA_ON)
@@ -1194,8 +1246,11 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
             prologue();
     };
     for (int i = 0; i < n_my; ++i) {
-        // K tile 0 has landed; K tile 1 may still be in flight
-        if (nk > 1)
+        // K tile 0 has landed; K tile 1 (and with a third stage, one operand of K tile 2) may
+        // still be in flight
+        if (DEEP != 0 && nk > 2)
+            wait_vmcnt<NDMA + L3>();
+        else if (nk > 1)
             wait_vmcnt<NDMA>();
         else
             wait_vmcnt<0>();
@@ -1209,7 +1264,11 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
         // needs K tile kt + 1, and the wait before it leaves nothing in flight, so the
         // deferred stores are complete at the barrier, like the DMA.  After it the stages of
         // K tile kt are free and are refilled with K tile kt + 2.
-        auto steady = [&](auto hook) {
+        // With a third stage for one operand (DEEP), that operand's rows run a step further
+        // ahead: the barrier of step kt needs K tile kt + 1 but leaves that operand's rows of
+        // K tile kt + 2 in flight, and after it the free stages take the other operand's rows
+        // of K tile kt + 2 and (`far`, while kt + 3 < nk) this operand's of K tile kt + 3.
+        auto steady = [&](auto hook, auto far) __attribute__((always_inline)) {
 #pragma unroll
             for (int s = 0; s + 1 < NSUB; ++s) {
                 if (s + 1 < NSPREAD && pending)
@@ -1220,10 +1279,26 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
                 interleave(s + 1 < NSPREAD ? PER : 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            wait_vmcnt<0>();
+            if constexpr (DEEP != 0)
+                wait_vmcnt<L3>();
+            else
+                wait_vmcnt<0>();
             barrier_no_fence();
             __builtin_amdgcn_sched_barrier(0);
-            issue_part_t(rw, rh, kt + NSTAGE, 0);
+            if constexpr (DEEP == 0) {
+                issue_part_t(rw, rh, kt + NSTAGE, 0);
+            } else if constexpr (DMA_ON) {
+                constexpr bool FAR = decltype(far)::value;
+                if constexpr (DEEP == 1) {
+                    issue_h(rh, kt + 2);
+                    if constexpr (FAR)
+                        issue_w(rw, kt + 3);
+                } else {
+                    issue_w(rw, kt + 2);
+                    if constexpr (FAR)
+                        issue_h(rh, kt + 3);
+                }
+            }
             pw = rw;
             ph = rh;
             pkt = kt + NSTAGE;
@@ -1240,19 +1315,28 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
             if (nk >= NSTAGE + DEFER) {
 #pragma unroll
                 for (int j = 0; j < DEFER; ++j)
-                    steady([&] {
+                    steady(
+                        [&] {
 #pragma unroll
-                        for (int q2 = 0; q2 < SPS; ++q2)
-                            store_one(NIMM + j * SPS + q2);
-                    });
+                            for (int q2 = 0; q2 < SPS; ++q2)
+                                store_one(NIMM + j * SPS + q2);
+                        },
+                        std::true_type{});
             } else {
 #pragma unroll
                 for (int j = NIMM; j < NST; ++j)
                     store_one(j);
             }
         }
-        while (kt + NSTAGE < nk)
-            steady([] {});
+        if constexpr (DEEP == 0) {
+            while (kt + NSTAGE < nk)
+                steady([] {}, std::true_type{});
+        } else {
+            while (kt + 3 < nk)
+                steady([] {}, std::true_type{});
+            if (kt + 2 < nk)
+                steady([] {}, std::false_type{});
+        }
         for (; kt < nk; ++kt) {
 #pragma unroll
             for (int s = 0; s + 1 < NSUB; ++s) {
@@ -1711,7 +1795,7 @@ hipError_t launch_persist(const void *H, const int32_t *idx, int64_t rows, const
 }
 
 template <int NSPREAD, int DEFER, int NIMM, bool STORE = true, bool REDUCE = false, bool M16 = false,
-          int DMAW = 8>
+          int DMAW = 8, int DEEP = 0>
 hipError_t launch_defer(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V, int64_t d,
                         void *out, int64_t ldo, int group_m, hipStream_t stream, float *pmax = nullptr,
                         int32_t *parg = nullptr, float *psum = nullptr)
@@ -1722,7 +1806,7 @@ hipError_t launch_defer(const void *H, const int32_t *idx, int64_t rows, const v
     const int64_t ntiles = ((V + 255) / 256) * ((rows + 255) / 256);
     int64_t grid = std::max<int64_t>(8, (cus / 8) * 8);
     grid = std::min<int64_t>(grid, ((ntiles + 7) / 8) * 8);
-    hipLaunchKernelGGL((gather_gemm_bf16_defer_kernel<NSPREAD, DEFER, NIMM, STORE, REDUCE, M16, DMAW>),
+    hipLaunchKernelGGL((gather_gemm_bf16_defer_kernel<NSPREAD, DEFER, NIMM, STORE, REDUCE, M16, DMAW, DEEP>),
                        dim3((unsigned)grid), dim3(512), 0, stream, (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V,
                        (int32_t)d, (__bf16 *)out, ldo, group_m, pmax, parg, psum);
     return hipGetLastError();
@@ -1760,6 +1844,7 @@ bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V)
     case kVariantBf16DeferS4I8:
     case kVariantBf16M16S1:
     case kVariantBf16M16Dma4:
+    case kVariantBf16M16Dma4W3:
         return ((rows + 255) / 256) * ((V + 255) / 256) <= 0x7fffffffLL;
     case kVariantBf16LowMShared:
         return rows <= 64;
@@ -1824,8 +1909,12 @@ hipError_t launch_gather_gemm(int variant, const void *H, const int32_t *idx, in
         return out_bf16 ? launch_defer<1, 1, 16, true, false, true>(H, idx, rows, W, V, d, out, ldo, group_m, stream)
                         : hipErrorInvalidValue;
     case kVariantBf16M16Dma4:
-        return out_bf16 ? launch_defer<1, 1, 16, true, false, true, 4>(H, idx, rows, W, V, d, out, ldo, group_m,
-                                                                      stream)
+        return out_bf16 ? launch_defer<1, 1, 16, true, false, true, 4, 0>(H, idx, rows, W, V, d, out, ldo, group_m,
+                                                                         stream)
+                        : hipErrorInvalidValue;
+    case kVariantBf16M16Dma4W3:
+        return out_bf16 ? launch_defer<1, 1, 16, true, false, true, 4, 1>(H, idx, rows, W, V, d, out, ldo, group_m,
+                                                                         stream)
                         : hipErrorInvalidValue;
     case kVariantBf16PersistK32:
         return launch_persist<32, 4, 2>(H, idx, rows, W, V, d, out, ldo, out_bf16, group_m, stream);

@@ -29,11 +29,13 @@ enum LogitsVariant : int {
                                    // every wave requests K tiles
     kVariantBf16LowMShared = 20,   // bf16, d % 64 == 0, M <= 64: W streaming with a workgroup-shared H tile
     kVariantBf16M16Dma4 = 21,      // bf16 -> bf16, d % 64 == 0: as 19, K tiles requested by one wave per
-                                   // SIMD (the bf16-output default)
+                                   // SIMD
+    kVariantBf16M16Dma4W3 = 22,    // as 21 with a third W stage (the bf16-output default)
 };
 
 // Default number of row tiles that share the W slabs of one XCD (tile order).
 constexpr int kDefaultGroupM = 8;
+
 
 
 // Whether a chunk of `rows` rows over V vocabulary rows fits the variant's launch grid.

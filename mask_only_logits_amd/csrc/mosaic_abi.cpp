@@ -140,6 +140,7 @@ bool variant_can_run(int v, int64_t M, int64_t d, mosaic_dtype_t in, mosaic_dtyp
     case mosaic::kVariantBf16W8K64S2: return bf16_in && d % 64 == 0 && small_d;
     case mosaic::kVariantBf16DeferS4I8:
     case mosaic::kVariantBf16M16S1:
+    case mosaic::kVariantBf16M16Dma4W3:
     case mosaic::kVariantBf16M16Dma4: return in == MOSAIC_BF16 && out == MOSAIC_BF16 && d % 64 == 0 && small_d;
     case mosaic::kVariantBf16PersistK32: return bf16_in && d % 32 == 0 && small_d;
     case mosaic::kVariantBf16LowMShared: return bf16_in && d % 64 == 0 && small_d && M <= 64;
@@ -159,8 +160,8 @@ int pick_variant(int64_t M, int64_t V, int64_t d, mosaic_dtype_t in, mosaic_dtyp
     // order, so the choice (made per launch from its row count) never changes a bit.
     if (variant_can_run(mosaic::kVariantBf16LowMShared, M, d, in, out))
         return mosaic::kVariantBf16LowMShared;
-    if (variant_can_run(mosaic::kVariantBf16M16Dma4, M, d, in, out))
-        return mosaic::kVariantBf16M16Dma4;
+    if (variant_can_run(mosaic::kVariantBf16M16Dma4W3, M, d, in, out))
+        return mosaic::kVariantBf16M16Dma4W3;
     if (variant_can_run(mosaic::kVariantBf16W8K64S2, M, d, in, out))
         return mosaic::kVariantBf16W8K64S2;
     if (variant_can_run(mosaic::kVariantBf16PersistK32, M, d, in, out))

@@ -57,8 +57,9 @@ def test_logits_bytes(m):
 def test_variant_choice(m):
     import torch
     bf, f32 = torch.bfloat16, torch.float32
-    assert m.mosaic_logits_variant(4096, 126464, 4096, bf, bf) == 21     # persistent, 16 x 16 x 32 MFMA
-    assert m.mosaic_logits_variant(65, 152064, 3584, bf, bf) == 21
+    assert m.mosaic_logits_variant(4096, 126464, 4096, bf, bf) == 22     # persistent, 16 x 16 x 32 MFMA
+    assert m.mosaic_logits_variant(65, 152064, 3584, bf, bf) == 22
+    assert m.mosaic_logits_variant(21399, 152064, 3584, bf, bf) == 22
     assert m.mosaic_logits_variant(4096, 126464, 4096, bf, f32) == 12    # 8-wave tiled kernel
     assert m.mosaic_logits_variant(20, 152064, 3584, bf, bf) == 20       # low-M streaming kernel, shared H
     assert m.mosaic_logits_variant(64, 152064, 3584, bf, f32) == 20

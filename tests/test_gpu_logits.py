@@ -93,8 +93,8 @@ def test_parity_lowm(m, lib_env, variant, dt_out, L, d, V, M):
 
 # every bf16 MFMA kernel form the library can select: persistent BK-32 (11), 8-wave tiled
 # (12), persistent 32 x 32 x 16 (16), persistent 16 x 16 x 32 with every wave requesting K
-# tiles (19) or one wave per SIMD (21), low-M streaming (20)
-BF16_MFMA_VARIANTS = (11, 12, 16, 19, 20, 21)
+# tiles (19) or one wave per SIMD (21; 22 with a third W stage), low-M streaming (20)
+BF16_MFMA_VARIANTS = (11, 12, 16, 19, 20, 21, 22)
 
 
 @pytest.mark.parametrize("M,d,V,out", [(20, 3584, 5000, "bf16"), (64, 256, 1001, "f32"), (700, 512, 1000, "bf16"),
@@ -104,7 +104,9 @@ BF16_MFMA_VARIANTS = (11, 12, 16, 19, 20, 21)
                                        (1024, 512, 65536, "bf16"), (1024, 64, 65536, "bf16"),
                                        (2048, 128, 32768, "bf16"),
                                        # low-M shapes with several blocks per wave
-                                       (20, 64, 131584, "bf16"), (64, 128, 40000, "f32"), (20, 64, 300000, "bf16")])
+                                       (20, 64, 131584, "bf16"), (64, 128, 40000, "f32"), (20, 64, 300000, "bf16"),
+                                       # 65 row tiles: a full super-group of 64 (XCDs side by side) + 1
+                                       (16500, 128, 2100, "bf16")])
 def test_bf16_variants_bit_identical(m, lib_env, M, d, V, out):
     # every bf16 MFMA variant accumulates each output in the same MFMA k order
     wl = inputs.make_random(M + d + V, L=max(M, 300), d=d, V=V, M=M, dtype="bf16")
@@ -115,12 +117,30 @@ def test_bf16_variants_bit_identical(m, lib_env, M, d, V, out):
         if v == 20 and M > 64:
             continue
         lib_env("MOSAIC_TUNE", f"variant={v}")
-        if out == "bf16" or v not in (16, 19, 21):  # the persistent deferred-store kernels write bf16 only
+        if out == "bf16" or v not in (16, 19, 21, 22):  # the persistent deferred-store kernels write bf16 only
             assert m.mosaic_logits_variant(M, V, d, torch.bfloat16, TD[out]) == v
         got = m.mosaic_masked_logits(H, idx_d, W, out_dtype=TD[out])
         torch.cuda.synchronize()
         assert torch.equal(got, ref), v
     lib_env("MOSAIC_TUNE", None)
+
+
+@pytest.mark.parametrize("group_m", [1, 2, 3, 8, 16])
+def test_tile_order_group_sizes(m, lib_env, group_m):
+    # The persistent kernels' tile lists (full super-groups of 8 * group_m row tiles with
+    # the XCDs side by side, then contiguous runs) must cover every tile once whatever the
+    # group size; the logits do not depend on it.
+    wl = inputs.make_random(31 + group_m, L=16600, d=128, V=1300, M=16500, dtype="bf16")
+    idx, idx_d = _gpu_idx(wl)
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    ref = m.mosaic_masked_logits(H, idx_d, W)
+    lib_env("MOSAIC_TUNE", f"group_m={group_m}")
+    got = m.mosaic_masked_logits(H, idx_d, W)
+    torch.cuda.synchronize()
+    lib_env("MOSAIC_TUNE", None)
+    assert torch.equal(got, ref)
+    rows = np.random.default_rng(group_m).choice(16500, 40, replace=False)
+    assert_close(got[torch.from_numpy(rows).to(DEV)], oracle.masked_logits(wl.H, idx[rows], wl.W), "group")
 
 
 @pytest.mark.parametrize("d,V,M", [(4096, 1000, 300), (512, 1001, 600), (72, 100, 50)])
