@@ -753,8 +753,8 @@ gather_gemm_bf16_persist_kernel(const __bf16 *__restrict__ H, const int32_t *__r
 // so a second batch is in flight while a step's H rows land: 3-7% faster (4096 x 4096 x
 // 126464: 1448-1452 against 1393-1395 TFLOP/s).  (With the XCDs out of step on large
 // launches it was 5-6% slower there; with the tile order below it is not.)  2 (H
-// three-deep instead) gained nothing.  REDUCE needs LDS beyond the five stages, so the
-// per-row consumer keeps two.
+// three-deep instead) gained nothing.  REDUCE with a third stage keeps its partials in the
+// W stage that is free at each tile's end (RED_IN_STAGE): 2-5% faster than two stages.
 template <int NSPREAD, int DEFER, int NIMM, bool STORE = true, bool REDUCE = false, bool M16 = false, int DMAW = 8,
           int DEEP = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
@@ -797,11 +797,19 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     // (wv = 1) of a tile, [3][BM] floats.  One LDS object: with a second one the compiler
     // can no longer tell the stage DMA from the fragment reads and waits for every DMA
     // before each read (measured 17% slower).
-    constexpr int RED_BYTES = REDUCE ? 3 * BM * 4 : 0;
+    // With a third W stage the five stages take all 160 KiB, and the partials live in the W
+    // stage that is free at the tile's end (RED_IN_STAGE, below).
+    constexpr bool RED_IN_STAGE = REDUCE && DEEP == 1;
+    constexpr int RED_BYTES = REDUCE && !RED_IN_STAGE ? 3 * BM * 4 : 0;
     static_assert(H_BASE + HST * H_TILE + RED_BYTES <= 160 * 1024, "LDS");
     static_assert(DEEP == 0 || (NSPREAD == 1 && M16 && NIMM == NST), "a third stage: 16 x 16 form, no deferral");
     __shared__ __attribute__((aligned(1024))) char smem[H_BASE + HST * H_TILE + RED_BYTES];
-    float *const red_lds = (float *)(smem + H_BASE + HST * H_TILE);
+    float *red_lds = (float *)(smem + H_BASE + HST * H_TILE);
+    // W stage of the current tile's K tile 0.  0 except with RED_IN_STAGE, where each tile's
+    // ring starts so that the next tile's K tile 2 lands in the stage that held this tile's
+    // partials: that request waits for the next tile's first barrier, after every wave has
+    // read them.
+    int w0 = 0;
 
     const int nvt = (V + BV - 1) / BV;
     const int nmt = (rows + BM - 1) / BM;
@@ -1218,13 +1226,15 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     };
 
     bf16x8_t af[2][AV], bf[2][AM];
-    // A tile's first two K tiles, in the order the waits count on: H0, W0, H1, W1
+    // A tile's first two K tiles, in the order the waits count on: H0, W0, H1, W1 (and W2 or
+    // H2 with a third stage; with RED_IN_STAGE, W2 after the tile's first barrier)
     auto prologue = [&]() __attribute__((always_inline)) {
         for (int s = 0; s < min(NSTAGE, nk); ++s)
 #pragma unroll
             for (int p = 0; p < NSPREAD; ++p)
-                issue_part(s * W_TILE, H_BASE + s * H_TILE, s, p);
-        if constexpr (DEEP == 1) {
+                issue_part((RED_IN_STAGE ? (w0 + s) % WST : s) * W_TILE, H_BASE + s * H_TILE, s, p);
+        if constexpr (RED_IN_STAGE) {
+        } else if constexpr (DEEP == 1) {
             if (nk > 2)
                 issue_w(2 * W_TILE, 2);
         } else if constexpr (DEEP == 2) {
@@ -1248,14 +1258,18 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     for (int i = 0; i < n_my; ++i) {
         // K tile 0 has landed; K tile 1 (and with a third stage, one operand of K tile 2) may
         // still be in flight
-        if (DEEP != 0 && nk > 2)
+        if (DEEP != 0 && !RED_IN_STAGE && nk > 2)
             wait_vmcnt<NDMA + L3>();
         else if (nk > 1)
             wait_vmcnt<NDMA>();
         else
             wait_vmcnt<0>();
         barrier_no_fence();
-        int rw = 0, rh = H_BASE;              // stages holding K tile kt
+        if constexpr (RED_IN_STAGE && DMA_ON) {
+            if (nk > 2)
+                issue_w(((w0 + 2) % WST) * W_TILE, 2);
+        }
+        int rw = (RED_IN_STAGE ? w0 : 0) * W_TILE, rh = H_BASE;   // stages holding K tile kt
         load_frags(rw, rh, 0, af[0], bf[0]);
         int pw = 0, ph = 0, pkt = 0, kt = 0;
         bool pending = false;
@@ -1369,6 +1383,13 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
         // every wave's last fragments are in registers: the stages are free
         int cm0, cv0;
         tile_coords(i, cm0, cv0);
+        if constexpr (RED_IN_STAGE) {
+            // the W stage of K tile nk - 2 (no wave reads it after that step's barrier, and
+            // no request targets it), or with one K tile a stage the tile never used
+            const int red_stage = (w0 + (nk >= 2 ? nk - 2 : 2)) % WST;
+            red_lds = (float *)(smem + red_stage * W_TILE);
+            w0 = (red_stage + 1) % WST;
+        }
         if constexpr (REDUCE)
             reduce_part1(cv0);
         wait_vmcnt<63>();
@@ -1862,10 +1883,10 @@ hipError_t launch_logits_argmax_lse(const void *H, const int32_t *idx, int64_t r
         group_m = kDefaultGroupM;
     hipError_t e;
     if (m16)
-        e = out ? launch_defer<1, 1, 16, true, true, true, 4>(H, idx, rows, W, V, d, out, ldo, group_m, stream,
-                                                              pmax, parg, psum)
-                : launch_defer<1, 1, 16, false, true, true, 4>(H, idx, rows, W, V, d, nullptr, ldo, group_m, stream,
-                                                               pmax, parg, psum);
+        e = out ? launch_defer<1, 1, 16, true, true, true, 4, 1>(H, idx, rows, W, V, d, out, ldo, group_m,
+                                                                 stream, pmax, parg, psum)
+                : launch_defer<1, 1, 16, false, true, true, 4, 1>(H, idx, rows, W, V, d, nullptr, ldo, group_m,
+                                                                  stream, pmax, parg, psum);
     else
         e = out ? launch_defer<2, 4, 8, true, true>(H, idx, rows, W, V, d, out, ldo, group_m, stream, pmax, parg, psum)
                 : launch_defer<2, 4, 8, false, true>(H, idx, rows, W, V, d, nullptr, ldo, group_m, stream, pmax, parg,
