@@ -192,6 +192,16 @@ def _find(root, suffix):
     return sorted(out)
 
 
+def _roofline_from_log(log_file: str) -> dict:
+    """The roofline object of the last JSON result line in a bench log ({} if none)."""
+    try:
+        with open(log_file, encoding="utf-8") as fh:
+            js = [ln for ln in fh if ln.startswith("{")]
+        return json.loads(js[-1]).get("roofline", {}) if js else {}
+    except (OSError, ValueError):
+        return {}
+
+
 def summarize_profile(root: str, workload: str, copy_mib: int, path: str = "logits", prof_dir: str | None = None):
     """Write profiles/ summaries from rocprofv3 output under `root`: kernel_stats
     (--kernel-trace --stats) and counter_collection (--pmc) CSV files.  `root/commands.txt`,
@@ -246,7 +256,10 @@ def summarize_profile(root: str, workload: str, copy_mib: int, path: str = "logi
         w_scale = known / (sum(cp["WRITE_SIZE"]) / len(cp["WRITE_SIZE"]) * 1024)
         fetch = sum(g["FETCH_SIZE"]) / len(g["FETCH_SIZE"]) * 1024 * f_scale
         write = sum(g["WRITE_SIZE"]) / len(g["WRITE_SIZE"]) * 1024 * w_scale
-        traffic = {"kernel_source_hash": kernel_source_hash(path), "workload": workload, "path": path,
+        # the hash of the sources the traced run was built from (as it reported it), so that
+        # summarising old output after a source change cannot attach it to the new code
+        traced = _roofline_from_log(os.path.join(root, "trace.log"))
+        traffic = {"kernel_source_hash": traced.get("kernel_source_hash"), "workload": workload, "path": path,
                    "bytes_per_launch": int(fetch + write), "fetch_bytes_per_launch": int(fetch),
                    "write_bytes_per_launch": int(write), "fetch_scale": f_scale, "write_scale": w_scale,
                    "copy_probe_bytes": known}
@@ -255,6 +268,10 @@ def summarize_profile(root: str, workload: str, copy_mib: int, path: str = "logi
         lines.append(f"L2-miss (L2-to-fabric, Infinity-Cache hits included) traffic per GEMM launch, scaled by "
                      f"the copy probe: fetch {fetch / 1e9:.3f} GB, write {write / 1e9:.3f} GB "
                      f"(scales {f_scale:.4f}, {w_scale:.4f})")
+        alg = traced.get("algorithmic_bytes_per_launch")
+        if alg:
+            lines.append(f"Algorithmic bytes per launch (from the traced run's JSON line): {alg / 1e9:.3f} GB; "
+                         f"L2-miss / algorithmic = {(fetch + write) / alg:.2f}")
     out = os.path.join(prof, f"gather_gemm_{tag}_rocprof.md")
     with open(out, "w", encoding="utf-8") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -460,7 +477,8 @@ def main():
                      "traffic_kind": "L2-miss bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a copy "
                                      "probe; Infinity-Cache hits included, so an upper bound on HBM bytes)",
                      "traffic_over_algorithmic": (round(traffic / (alg_bytes / launches), 3)
-                                                  if traffic is not None else None)})
+                                                  if traffic is not None else None),
+                     "kernel_source_hash": kernel_source_hash(args.path)})
     result = {
         "metric": METRIC,
         "value": round(value, 3),

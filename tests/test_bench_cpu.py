@@ -52,6 +52,11 @@ def test_summarize_profile_scales_by_the_copy_probe(tmp_path):
     _write_csv(str(raw / "write" / "write_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
                [[gemm, "WRITE_SIZE", 500], [gemm, "WRITE_SIZE", 500]] + [[copy, "WRITE_SIZE", known / 1024]] * 3)
     (raw / "commands.txt").write_text("rocprofv3 --kernel-trace --stats -- python3 bench.py\n")
+    # the traced run's own result line: its source hash and algorithmic bytes are what the
+    # summary keeps (not the hash of the sources present when it is summarised)
+    (raw / "trace.log").write_text("[bench] noise\n" + json.dumps(
+        {"roofline": {"kernel_source_hash": bench.kernel_source_hash(),
+                      "algorithmic_bytes_per_launch": 1000 * 1024}}) + "\n")
     os.makedirs(prof)
     bench.summarize_profile(str(raw), "wl", copy_mib, "logits", prof_dir=str(prof))
 
@@ -63,12 +68,18 @@ def test_summarize_profile_scales_by_the_copy_probe(tmp_path):
     assert t["kernel_source_hash"] == bench.kernel_source_hash()
     md = (prof / "gather_gemm_wl_rocprof.md").read_text()
     assert "rocprofv3 --kernel-trace --stats" in md and "| 4 | 12.000 | 3000.0 |" in md
+    assert "L2-miss / algorithmic = 4.50" in md     # (2000 * 2 + 500) KiB over 1000 KiB
 
     assert bench.measured_traffic("wl", "logits", prof_dir=str(prof)) == t["bytes_per_launch"]
     t["kernel_source_hash"] = "0" * 16
     (prof / "traffic_gather_gemm_wl.json").write_text(json.dumps(t))
     assert bench.measured_traffic("wl", "logits", prof_dir=str(prof)) is None
     assert bench.measured_traffic("absent", "logits", prof_dir=str(prof)) is None
+
+    # output of a run on other sources keeps that run's hash, so it never matches these
+    (raw / "trace.log").write_text(json.dumps({"roofline": {"kernel_source_hash": "f" * 16}}) + "\n")
+    bench.summarize_profile(str(raw), "wl", copy_mib, "logits", prof_dir=str(prof))
+    assert bench.measured_traffic("wl", "logits", prof_dir=str(prof)) is None
 
 
 def test_source_hash_follows_the_paths_kernels():
