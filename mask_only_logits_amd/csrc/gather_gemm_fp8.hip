@@ -434,6 +434,280 @@ gather_gemm_fp8_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__
 }
 
 
+// The FP8 GEMM's default form: the tile, fragments, MFMA sequence and epilogue of
+// gather_gemm_fp8_kernel<8> (so the logits are bit-identical to it), with the K pipeline
+// of the bf16 persistent kernel's default:
+//  * only waves 0-3, one per SIMD, request K tiles (a quarter each); waves 4-7 run a copy
+//    of the K loop with no requests, so each SIMD has one wave whose MFMA issue is never
+//    held up by the texture path;
+//  * W has three LDS stages and H two (160 KiB): at step k's barrier H's rows of K tile
+//    k + 2 are requested into the H stage just freed, and W's rows of K tile k + 3 into the
+//    freed W stage at the start of the next step, so each wait leaves one W K tile in
+//    flight and W's requests have two steps to land;
+//  * the 2 KiB of row scales no longer fit beside the stages: they are requested into the
+//    W stage that K tile nk - 2 frees (a stage the tile never uses when nk == 1) and waited
+//    for before the epilogue.
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
+gather_gemm_fp8_w3_kernel(const uint8_t *__restrict__ Hq, const float *__restrict__ hs, int32_t rows,
+                          const uint8_t *__restrict__ Wq, const float *__restrict__ ws, int32_t V, int32_t d,
+                          __bf16 *__restrict__ out, int64_t ldo, int32_t group_m)
+{
+    constexpr int NW = 8, DMAW = 4;
+    constexpr int BV = 256, BM = 256, BK = 128, WST = 3, HST = 2;
+    constexpr int ROW_BYTES = BK;             // one byte per code
+    constexpr int CHUNKS = ROW_BYTES / 16, RPI = 64 / CHUNKS;
+    constexpr int W_TILE = BV * ROW_BYTES, H_TILE = BM * ROW_BYTES;
+    constexpr int H_BASE = WST * W_TILE;
+    constexpr int WV = BV / 2, WM = BM / (NW / 2);
+    constexpr int AV = WV / 32, AM = WM / 32;
+    constexpr int LW = BV / RPI / DMAW, LH = BM / RPI / DMAW;   // requests per requesting wave
+    constexpr int NDMA = LW + LH;
+    static_assert(H_BASE + HST * H_TILE <= 160 * 1024, "LDS");
+    static_assert(BV == BM, "scale staging assumes square tiles");
+    __shared__ __attribute__((aligned(1024))) char smem[H_BASE + HST * H_TILE];
+
+    const int nvt = (V + BV - 1) / BV;
+    const int nmt = (rows + BM - 1) / BM;
+    const int nblk = nvt * nmt;
+    // XCD-aware renumbering and grouped order, as in gather_gemm_fp8_kernel
+    const int b = blockIdx.x;
+    const int qq = nblk >> 3, rem = nblk & 7, xcd = b & 7, slot = b >> 3;
+    const int t = (xcd < rem ? xcd * (qq + 1) : rem * (qq + 1) + (xcd - rem) * qq) + slot;
+    const int per_group = group_m * nvt;
+    const int g = t / per_group;
+    const int first_m = g * group_m;
+    const int gsz = min(nmt - first_m, group_m);
+    const int local = t - g * per_group;
+    const int m0 = (first_m + local % gsz) * BM;
+    const int v0 = (local / gsz) * BV;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wv = wave & 1, wm = wave >> 1;
+    const bool dma_wave = wave < DMAW;
+    const int dwave = wave % DMAW;
+    auto swz = [](int r) { return (r >> 1) & 7; };
+
+    // DMA sources of a requesting wave (layout as in gather_gemm_fp8_kernel)
+    const uint8_t *wsrc[LW];
+    const uint8_t *hsrc[LH];
+#pragma unroll
+    for (int j = 0; j < LW; ++j) {
+        const int r = (dwave * LW + j) * RPI + lane / CHUNKS;
+        wsrc[j] = Wq + (int64_t)min(v0 + r, V - 1) * d + ((lane % CHUNKS) ^ swz(r)) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < LH; ++j) {
+        const int r = (dwave * LH + j) * RPI + lane / CHUNKS;
+        hsrc[j] = Hq + (int64_t)min(m0 + r, rows - 1) * d + ((lane % CHUNKS) ^ swz(r)) * 16;
+    }
+    auto issue_w = [&](int rw, int kt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < LW; ++j)
+            __builtin_amdgcn_global_load_lds((const void *)(wsrc[j] + kt * ROW_BYTES),
+                                             (lds_void_t *)(smem + rw + (dwave * LW + j) * 1024), 16, 0, 0);
+    };
+    auto issue_h = [&](int rh, int kt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < LH; ++j)
+            __builtin_amdgcn_global_load_lds((const void *)(hsrc[j] + kt * ROW_BYTES),
+                                             (lds_void_t *)(smem + rh + (dwave * LH + j) * 1024), 16, 0, 0);
+    };
+    // the tile's row scales (W's 256, then H's 256, fp32; indices clamped to the last valid
+    // row, whose copies are never used): instructions dwave and dwave + 4 of 8
+    auto issue_scales = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = dwave; j < 8; j += DMAW) {
+            const float *src = j < 4 ? ws + min(v0 + j * 64 + lane, V - 1) : hs + min(m0 + (j - 4) * 64 + lane, rows - 1);
+            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_t *)(smem + base + j * 256), 4, 0, 0);
+        }
+    };
+
+    f32x16_t acc[AV][AM];
+#pragma unroll
+    for (int a = 0; a < AV; ++a)
+#pragma unroll
+        for (int bm = 0; bm < AM; ++bm)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[a][bm][e] = 0.0f;
+
+    const int fr = lane & 31, hi = lane >> 5;
+    const int lane_chunk = ((2 * hi) ^ swz(fr)) * 16;
+    const int a_addr = (wv * WV + fr) * ROW_BYTES + lane_chunk;   // from a W stage
+    const int b_addr = (wm * WM + fr) * ROW_BYTES + lane_chunk;   // from an H stage
+    auto frag = [&](int addr, int s) __attribute__((always_inline)) {
+        const i32x4_t lo = *(const i32x4_t *)(smem + (addr ^ (64 * s)));
+        const i32x4_t up = *(const i32x4_t *)(smem + (addr ^ (64 * s + 16)));
+        return i32x8_t{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+    };
+    // MFMAs on B fragment buffer `cur` while sub-step s of the stages at rw (W) and rh (H)
+    // is read: the B fragments first, then each block's next A fragment after its row's
+    // MFMAs (as gather_gemm_fp8_kernel<8>)
+    auto mma_load = [&](int rw, int rh, int s, int cur, i32x8_t (&af)[AV], i32x8_t (&bf)[2][AM])
+                        __attribute__((always_inline)) {
+#pragma unroll
+        for (int bm = 0; bm < AM; ++bm)
+            bf[cur ^ 1][bm] = frag(b_addr + rh + bm * 32 * ROW_BYTES, s);
+#pragma unroll
+        for (int a = 0; a < AV; ++a) {
+#pragma unroll
+            for (int bm = 0; bm < AM; ++bm)
+                acc[a][bm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[a], bf[cur][bm], acc[a][bm], 0, 0, 0,
+                                                                             127, 0, 127);
+            af[a] = frag(a_addr + rw + a * 32 * ROW_BYTES, s);
+        }
+    };
+    auto interleave = [&](int nvm) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            if (i < nvm) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+        }
+#pragma unroll
+        for (int bm = 0; bm < AM; ++bm) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        const int used = nvm + AM;
+#pragma unroll
+        for (int a = 0; a < AV; ++a) {
+#pragma unroll
+            for (int c = 0; c < AM; ++c)
+                if (a * AM + c >= used)
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+    };
+    auto next_w = [](int rw) { return rw + W_TILE == WST * W_TILE ? 0 : rw + W_TILE; };
+    auto next_h = [](int rh) { return rh + H_TILE == H_BASE + HST * H_TILE ? H_BASE : rh + H_TILE; };
+
+    const int nk = d / BK;
+    const int sc_stage = nk >= 2 ? (nk - 2) % WST : 2;
+    i32x8_t af[AV], bf[2][AM];
+    auto k_loop = [&](auto dma_tag) __attribute__((always_inline)) {
+        constexpr bool DMA_ON = decltype(dma_tag)::value;
+        // H0, W0, H1, W1, W2 (the order the waits count on)
+        if constexpr (DMA_ON) {
+            issue_h(H_BASE, 0);
+            issue_w(0, 0);
+            if (nk > 1) {
+                issue_h(H_BASE + H_TILE, 1);
+                issue_w(W_TILE, 1);
+            }
+            if (nk > 2)
+                issue_w(2 * W_TILE, 2);
+            else if (nk == 1)
+                issue_scales(2 * W_TILE);
+        }
+        if (nk > 2)
+            wait_vm<NDMA + LW>();
+        else if (nk == 2)
+            wait_vm<NDMA>();
+        else
+            wait_vm<0>();
+        bar();
+#pragma unroll
+        for (int a = 0; a < AV; ++a)
+            af[a] = frag(a_addr + a * 32 * ROW_BYTES, 0);
+#pragma unroll
+        for (int bm = 0; bm < AM; ++bm)
+            bf[0][bm] = frag(b_addr + H_BASE + bm * 32 * ROW_BYTES, 0);
+        int rw = 0, rh = H_BASE, kt = 0, pw = 0, pkt = 0;
+        bool pend_w = false;
+        for (; kt + 2 < nk; ++kt) {
+            // sub-step 0: W's rows of K tile kt + 2 (requested for the stage the previous
+            // barrier freed), the fragments of sub-step 1
+            if (DMA_ON && pend_w)
+                issue_w(pw, pkt);
+            mma_load(rw, rh, 1, 0, af, bf);
+            interleave(DMA_ON && pend_w ? LW : 0);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm<LW>();   // K tile kt + 1 has landed; W's K tile kt + 2 may not have
+            bar();
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (DMA_ON)
+                issue_h(rh, kt + 2);
+            pend_w = kt + 3 < nk;
+            pw = rw;
+            pkt = kt + 3;
+            const int nxw = next_w(rw), nxh = next_h(rh);
+            mma_load(nxw, nxh, 0, 1, af, bf);
+            interleave(DMA_ON ? LH : 0);
+            __builtin_amdgcn_sched_barrier(0);
+            rw = nxw;
+            rh = nxh;
+        }
+        for (; kt < nk; ++kt) {
+            mma_load(rw, rh, 1, 0, af, bf);
+            // one MFMA sequence for both cases; after the last K tile its reads are unused
+            if (kt + 1 < nk) {
+                wait_vm<0>();
+                bar();
+                if constexpr (DMA_ON) {
+                    if (kt == nk - 2)
+                        issue_scales(rw);   // the W stage of K tile nk - 2, free now
+                }
+                rw = next_w(rw);
+                rh = next_h(rh);
+            }
+            mma_load(rw, rh, 0, 1, af, bf);
+        }
+    };
+    if (dma_wave)
+        k_loop(std::true_type{});
+    else
+        k_loop(std::false_type{});
+    wait_vm<0>();
+    bar();   // every requesting wave's scales have landed
+
+    // epilogue as in gather_gemm_fp8_kernel
+    auto pack2 = [](float x, float y) {
+        const __bf16 a = static_cast<__bf16>(x), b = static_cast<__bf16>(y);
+        return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    };
+    const bool vec_ok = ((uintptr_t)out & 15) == 0 && (ldo & 7) == 0;
+    const float *sc = (const float *)(smem + sc_stage * W_TILE);
+#pragma unroll
+    for (int bm = 0; bm < AM; ++bm) {
+        const int row = m0 + wm * WM + bm * 32 + fr;
+        const bool row_ok = row < rows;
+        const float h = sc[BV + wm * WM + bm * 32 + fr];
+#pragma unroll
+        for (int a = 0; a < AV; ++a) {
+            const int vb = v0 + wv * WV + a * 32;
+            uint32_t pk[4][2];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int v = vb + gq * 8 + hi * 4;
+                const f32x4_t w = *(const f32x4_t *)(sc + (v - v0));
+                pk[gq][0] = pack2(acc[a][bm][gq * 4 + 0] * (h * w[0]), acc[a][bm][gq * 4 + 1] * (h * w[1]));
+                pk[gq][1] = pack2(acc[a][bm][gq * 4 + 2] * (h * w[2]), acc[a][bm][gq * 4 + 3] * (h * w[3]));
+            }
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                const auto s0 = __builtin_amdgcn_permlane32_swap(pk[2 * pr][0], pk[2 * pr + 1][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(pk[2 * pr][1], pk[2 * pr + 1][1], false, false);
+                const int v = vb + 16 * pr + 8 * hi;
+                if (!row_ok)
+                    continue;   // (after the swaps: every lane takes part in them)
+                __bf16 *o = out + (int64_t)row * ldo + v;
+                if (vec_ok && v + 7 < V) {
+                    *(uint4 *)o = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+                } else {
+                    const uint32_t w4[4] = {s0[0], s1[0], s0[1], s1[1]};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (v + e < V)
+                            o[e] = __builtin_bit_cast(__bf16, (uint16_t)(w4[e >> 1] >> (16 * (e & 1))));
+                }
+            }
+        }
+    }
+}
+
 // Low-M FP8 logits (rows <= 32 * AM): streaming the W codes once.
 // The bf16 low-M kernel's design with fp8 operands:
 //  * wave w of the grid owns an equal, contiguous range of vocabulary rows (the
@@ -634,8 +908,11 @@ hipError_t launch_gemm_fp8(const uint8_t *Hq, const float *hs, int64_t rows, con
     if (nwaves == 4)
         hipLaunchKernelGGL(gather_gemm_fp8_kernel<4>, dim3((unsigned)nblk), dim3(256), 0, stream, Hq, hs,
                            (int32_t)rows, Wq, ws, (int32_t)V, (int32_t)d, (__bf16 *)out, ldo, group_m);
-    else
+    else if (nwaves == 8)
         hipLaunchKernelGGL(gather_gemm_fp8_kernel<8>, dim3((unsigned)nblk), dim3(512), 0, stream, Hq, hs,
+                           (int32_t)rows, Wq, ws, (int32_t)V, (int32_t)d, (__bf16 *)out, ldo, group_m);
+    else
+        hipLaunchKernelGGL(gather_gemm_fp8_w3_kernel, dim3((unsigned)nblk), dim3(512), 0, stream, Hq, hs,
                            (int32_t)rows, Wq, ws, (int32_t)V, (int32_t)d, (__bf16 *)out, ldo, group_m);
     return hipGetLastError();
 }

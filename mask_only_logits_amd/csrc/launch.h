@@ -64,7 +64,9 @@ hipError_t launch_quantize_rows_e4m3(const void *X, bool in_bf16, int64_t d, con
                                      uint8_t *q, float *scale, hipStream_t stream);
 
 // out[i, v] (bf16) = (sum_k Hq[i, k] Wq[v, k]) * hs[i] * ws[v] for i < rows, v < V;
-// d % 128 == 0; nwaves 4 or 8.
+// d % 128 == 0; nwaves 4 or 8: the comparison forms with every wave requesting K tiles,
+// anything else: the default (eight waves, four requesting, three W stages).  All three
+// give the same bits.
 hipError_t launch_gemm_fp8(const uint8_t *Hq, const float *hs, int64_t rows, const uint8_t *Wq, const float *ws,
                            int64_t V, int64_t d, void *out, int64_t ldo, int group_m, int nwaves, hipStream_t stream);
 

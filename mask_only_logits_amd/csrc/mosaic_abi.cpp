@@ -47,14 +47,16 @@ int64_t checked_bytes(int64_t rows, int64_t V, int64_t esize)
 
 // Debug/tuning override, read from the environment once per process (the first call
 // that needs it) and again on mosaic_debug_reload_env():
-// MOSAIC_TUNE="variant=<n>,group_m=<g>,waves=<w>,fp8lowm=0" (waves: the FP8 kernel's 4 or
-// 8; fp8lowm=0: FP8 chunks of at most 64 rows also take the tiled FP8 kernel).
+// MOSAIC_TUNE="variant=<n>,group_m=<g>,waves=<w>,fp8lowm=0" (waves=4 or 8: the FP8 GEMM's
+// comparison forms with every wave requesting K tiles, one or two waves per SIMD; default:
+// eight waves, four requesting, three W stages; fp8lowm=0: FP8 chunks of at most 64 rows
+// also take the tiled FP8 kernel).
 // A forced variant that cannot run the call's shape is ignored.  For the fused consumer,
 // variant=16 selects its 32 x 32 x 16 MFMA form (default: 16 x 16 x 32).
 struct Tune {
     int variant = -1;
     int group_m = 0;
-    int waves = 8;   // FP8 kernel: two waves per SIMD, measured 1% faster than one
+    int waves = 0;   // FP8 GEMM form: 0 = default, 4 or 8 = comparison forms
     bool fp8_lowm = true;   // FP8 chunks of at most 64 rows take the W-streaming kernel
     bool check_idx = false;   // MOSAIC_CHECK_IDX=1
 };
@@ -72,8 +74,8 @@ Tune parse_env()
         t.variant = atoi(p + 8);
     if ((p = strstr(e, "group_m=")))
         t.group_m = atoi(p + 8);
-    if ((p = strstr(e, "waves=")) && atoi(p + 6) == 4)
-        t.waves = 4;
+    if ((p = strstr(e, "waves=")) && (atoi(p + 6) == 4 || atoi(p + 6) == 8))
+        t.waves = atoi(p + 6);
     if ((p = strstr(e, "fp8lowm=")) && atoi(p + 8) == 0)
         t.fp8_lowm = false;
     return t;

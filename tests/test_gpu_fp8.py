@@ -66,15 +66,16 @@ def test_parity_random(m, L, d, V, M, C):
     assert_close(out, ref, f"fp8 {L},{d},{V},{M},{C}")
 
 
-def test_chunked_waves_and_determinism(m, lib_env):
-    wl = inputs.make_random(55, L=1500, d=256, V=2000, M=1100, dtype="bf16")
+@pytest.mark.parametrize("d", [128, 256, 384, 1024])   # 1, 2, 3 and 8 K tiles
+def test_chunked_waves_and_determinism(m, lib_env, d):
+    wl = inputs.make_random(55 + d, L=1500, d=d, V=2000, M=1100, dtype="bf16")
     idx_d = torch.from_numpy(oracle.mask_compact(wl.tokens, wl.mask_id)).to(DEV)
     H = wl.H.to(DEV)
     Wq, ws = m.mosaic_quantize_rows_fp8(wl.W.to(DEV))
     ref = m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws)
     for C in (1, 64, 255, 256, 300, 1099, -1):
         assert torch.equal(m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws, chunk_rows=C), ref), C
-    for tune in ("waves=4",):
+    for tune in ("waves=4", "waves=8"):   # the comparison forms; the default is the three-stage one
         lib_env("MOSAIC_TUNE", tune)
         assert torch.equal(m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws), ref), tune
         assert torch.equal(m.mosaic_masked_logits_fp8(H, idx_d, Wq, ws, chunk_rows=300), ref), tune
