@@ -747,16 +747,19 @@ gather_gemm_bf16_persist_kernel(const __bf16 *__restrict__ H, const int32_t *__r
 // Measured on 4096 rows x 4096 x 126464: moving one launch's K tiles alone takes 1.76 ms
 // with 4 requesting waves and 1.94 ms with 8; the GEMM runs 3-5% faster; bit-identical.
 //
-// DEEP: 0: two LDS stages per operand, so the refill issued at step kt's barrier must land
-// by the next one (a single batch of requests in flight, and the texture path idles between
-// batches).  1: W gets a third stage (160 KiB of LDS in all) and runs a step further ahead,
-// so a second batch is in flight while a step's H rows land: 3-7% faster (4096 x 4096 x
-// 126464: 1448-1452 against 1393-1395 TFLOP/s).  (With the XCDs out of step on large
-// launches it was 5-6% slower there; with the tile order below it is not.)  2 (H
-// three-deep instead) gained nothing.  REDUCE with a third stage keeps its partials in the
-// W stage that is free at each tile's end (RED_IN_STAGE): 2-5% faster than two stages.
+// DEEP: false: two LDS stages per operand, so the refill issued at step kt's barrier must
+// land by the next one (a single batch of requests in flight, and the texture path idles
+// between batches).  true: W gets a third stage (160 KiB of LDS in all).  Step kt requests
+// W's rows of K tile kt + 2 at its start and H's after its barrier, so W's requests are in
+// flight while H's land, and a step's 16 requests are split over its two halves: 3-7%
+// faster (4096 x 4096 x 126464: 1448-1452 against 1393-1395 TFLOP/s with W's requested at
+// the barrier, K tile kt + 3; requesting them at the next step's start instead gained
+// 0.3-1.8% more).  (With the XCDs out of step on large launches it was 5-6% slower there;
+// with the tile order below it is not.)  A third H stage instead gained nothing.  REDUCE
+// with a third stage keeps its partials in the W stage that is free at each tile's end
+// (RED_IN_STAGE): 2-5% faster than two stages.
 template <int NSPREAD, int DEFER, int NIMM, bool STORE = true, bool REDUCE = false, bool M16 = false, int DMAW = 8,
-          int DEEP = 0>
+          bool DEEP = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
 gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict__ idx, int32_t rows,
                               const __bf16 *__restrict__ W, int32_t V, int32_t d, __bf16 *__restrict__ out,
@@ -764,7 +767,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
                               int32_t *__restrict__ parg, float *__restrict__ psum)
 {
     constexpr int NW = 8, BV = 256, BM = 256, BK = 64, NSTAGE = 2;
-    constexpr int WST = DEEP == 1 ? 3 : 2, HST = DEEP == 2 ? 3 : 2;   // W and H stages
+    constexpr int WST = DEEP ? 3 : 2, HST = 2;   // W and H stages
     constexpr int ROW_BYTES = BK * 2;
     constexpr int CHUNKS = BK / 8;
     constexpr int RPI = 64 / CHUNKS;
@@ -780,7 +783,6 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     constexpr int NACC = MB * MB / 64;        // accumulators per lane and block
     constexpr int AV = WV / MB, AM = WM / MB;
     constexpr int LW = BV / RPI / DMAW, LH = BM / RPI / DMAW;   // DMA instructions of a DMA wave
-    constexpr int L3 = DEEP == 1 ? LW : DEEP == 2 ? LH : 0;    // those of the operand with a third stage
     constexpr int NSUB = BK / KI;
     constexpr int NDMA = LW + LH;
     constexpr int NFR = AV + AM;
@@ -799,10 +801,10 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     // before each read (measured 17% slower).
     // With a third W stage the five stages take all 160 KiB, and the partials live in the W
     // stage that is free at the tile's end (RED_IN_STAGE, below).
-    constexpr bool RED_IN_STAGE = REDUCE && DEEP == 1;
+    constexpr bool RED_IN_STAGE = REDUCE && DEEP;
     constexpr int RED_BYTES = REDUCE && !RED_IN_STAGE ? 3 * BM * 4 : 0;
     static_assert(H_BASE + HST * H_TILE + RED_BYTES <= 160 * 1024, "LDS");
-    static_assert(DEEP == 0 || (NSPREAD == 1 && M16 && NIMM == NST), "a third stage: 16 x 16 form, no deferral");
+    static_assert(!DEEP || (NSPREAD == 1 && M16 && NIMM == NST), "a third stage: 16 x 16 form, no deferral");
     __shared__ __attribute__((aligned(1024))) char smem[H_BASE + HST * H_TILE + RED_BYTES];
     float *red_lds = (float *)(smem + H_BASE + HST * H_TILE);
     // W stage of the current tile's K tile 0.  0 except with RED_IN_STAGE, where each tile's
@@ -1226,21 +1228,13 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     };
 
     bf16x8_t af[2][AV], bf[2][AM];
-    // A tile's first two K tiles, in the order the waits count on: H0, W0, H1, W1 (and W2 or
-    // H2 with a third stage; with RED_IN_STAGE, W2 after the tile's first barrier)
+    // A tile's first two K tiles, in the order the waits count on: H0, W0, H1, W1 (with a third
+    // stage, W2 is requested by the tile's first step, after the tile's first barrier)
     auto prologue = [&]() __attribute__((always_inline)) {
         for (int s = 0; s < min(NSTAGE, nk); ++s)
 #pragma unroll
             for (int p = 0; p < NSPREAD; ++p)
                 issue_part((RED_IN_STAGE ? (w0 + s) % WST : s) * W_TILE, H_BASE + s * H_TILE, s, p);
-        if constexpr (RED_IN_STAGE) {
-        } else if constexpr (DEEP == 1) {
-            if (nk > 2)
-                issue_w(2 * W_TILE, 2);
-        } else if constexpr (DEEP == 2) {
-            if (nk > 2)
-                issue_h(H_BASE + 2 * H_TILE, 2);
-        }
     };
     if (dma_wave)
         prologue();
@@ -1256,19 +1250,12 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
             prologue();
     };
     for (int i = 0; i < n_my; ++i) {
-        // K tile 0 has landed; K tile 1 (and with a third stage, one operand of K tile 2) may
-        // still be in flight
-        if (DEEP != 0 && !RED_IN_STAGE && nk > 2)
-            wait_vmcnt<NDMA + L3>();
-        else if (nk > 1)
+        // K tile 0 has landed; K tile 1 may still be in flight
+        if (nk > 1)
             wait_vmcnt<NDMA>();
         else
             wait_vmcnt<0>();
         barrier_no_fence();
-        if constexpr (RED_IN_STAGE && DMA_ON) {
-            if (nk > 2)
-                issue_w(((w0 + 2) % WST) * W_TILE, 2);
-        }
         int rw = (RED_IN_STAGE ? w0 : 0) * W_TILE, rh = H_BASE;   // stages holding K tile kt
         load_frags(rw, rh, 0, af[0], bf[0]);
         int pw = 0, ph = 0, pkt = 0, kt = 0;
@@ -1278,48 +1265,42 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
         // needs K tile kt + 1, and the wait before it leaves nothing in flight, so the
         // deferred stores are complete at the barrier, like the DMA.  After it the stages of
         // K tile kt are free and are refilled with K tile kt + 2.
-        // With a third stage for one operand (DEEP), that operand's rows run a step further
-        // ahead: the barrier of step kt needs K tile kt + 1 but leaves that operand's rows of
-        // K tile kt + 2 in flight, and after it the free stages take the other operand's rows
-        // of K tile kt + 2 and (`far`, while kt + 3 < nk) this operand's of K tile kt + 3.
-        auto steady = [&](auto hook, auto far) __attribute__((always_inline)) {
+        // With a third W stage (DEEP), W's rows run a step further ahead: step kt requests W's
+        // rows of K tile kt + 2 at its start, into the stage K tile kt - 1 freed at the last
+        // barrier, and H's rows of K tile kt + 2 after its own barrier; that barrier's wait
+        // needs K tile kt + 1 and leaves W's K tile kt + 2 in flight.
+        auto steady = [&](auto hook) __attribute__((always_inline)) {
 #pragma unroll
             for (int s = 0; s + 1 < NSUB; ++s) {
                 if (s + 1 < NSPREAD && pending)
                     issue_part_t(pw, ph, pkt, s + 1);
+                if constexpr (DEEP && DMA_ON) {
+                    if (s == 0)
+                        issue_w(next_w(next_w(rw)), kt + 2);
+                }
                 if (s == HOOK_S)
                     hook();
                 mma_load(rw, rh, s + 1, s & 1, af, bf);
-                interleave(s + 1 < NSPREAD ? PER : 0);
+                interleave(s + 1 < NSPREAD ? PER : (DEEP && DMA_ON && s == 0 ? LW : 0));
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (DEEP != 0)
-                wait_vmcnt<L3>();
+            if constexpr (DEEP)
+                wait_vmcnt<LW>();
             else
                 wait_vmcnt<0>();
             barrier_no_fence();
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (DEEP == 0) {
+            if constexpr (!DEEP)
                 issue_part_t(rw, rh, kt + NSTAGE, 0);
-            } else if constexpr (DMA_ON) {
-                constexpr bool FAR = decltype(far)::value;
-                if constexpr (DEEP == 1) {
-                    issue_h(rh, kt + 2);
-                    if constexpr (FAR)
-                        issue_w(rw, kt + 3);
-                } else {
-                    issue_w(rw, kt + 2);
-                    if constexpr (FAR)
-                        issue_h(rh, kt + 3);
-                }
-            }
+            else if constexpr (DMA_ON)
+                issue_h(rh, kt + 2);
             pw = rw;
             ph = rh;
             pkt = kt + NSTAGE;
             pending = NSPREAD > 1;
             const int nxw = next_w(rw), nxh = next_h(rh);
             mma_load(nxw, nxh, 0, (NSUB - 1) & 1, af, bf);
-            interleave(PER);
+            interleave(DEEP ? (DMA_ON ? LH : 0) : PER);
             __builtin_amdgcn_sched_barrier(0);
             rw = nxw;
             rh = nxh;
@@ -1329,28 +1310,19 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
             if (nk >= NSTAGE + DEFER) {
 #pragma unroll
                 for (int j = 0; j < DEFER; ++j)
-                    steady(
-                        [&] {
+                    steady([&] {
 #pragma unroll
-                            for (int q2 = 0; q2 < SPS; ++q2)
-                                store_one(NIMM + j * SPS + q2);
-                        },
-                        std::true_type{});
+                        for (int q2 = 0; q2 < SPS; ++q2)
+                            store_one(NIMM + j * SPS + q2);
+                    });
             } else {
 #pragma unroll
                 for (int j = NIMM; j < NST; ++j)
                     store_one(j);
             }
         }
-        if constexpr (DEEP == 0) {
-            while (kt + NSTAGE < nk)
-                steady([] {}, std::true_type{});
-        } else {
-            while (kt + 3 < nk)
-                steady([] {}, std::true_type{});
-            if (kt + 2 < nk)
-                steady([] {}, std::false_type{});
-        }
+        while (kt + NSTAGE < nk)
+            steady([] {});
         for (; kt < nk; ++kt) {
 #pragma unroll
             for (int s = 0; s + 1 < NSUB; ++s) {
@@ -1834,7 +1806,7 @@ hipError_t launch_persist(const void *H, const int32_t *idx, int64_t rows, const
 }
 
 template <int NSPREAD, int DEFER, int NIMM, bool STORE = true, bool REDUCE = false, bool M16 = false,
-          int DMAW = 8, int DEEP = 0>
+          int DMAW = 8, bool DEEP = false>
 hipError_t launch_defer(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V, int64_t d,
                         void *out, int64_t ldo, int group_m, hipStream_t stream, float *pmax = nullptr,
                         int32_t *parg = nullptr, float *psum = nullptr)
@@ -1901,9 +1873,9 @@ hipError_t launch_logits_argmax_lse(const void *H, const int32_t *idx, int64_t r
         group_m = kDefaultGroupM;
     hipError_t e;
     if (m16)
-        e = out ? launch_defer<1, 1, 16, true, true, true, 4, 1>(H, idx, rows, W, V, d, out, ldo, group_m,
+        e = out ? launch_defer<1, 1, 16, true, true, true, 4, true>(H, idx, rows, W, V, d, out, ldo, group_m,
                                                                  stream, pmax, parg, psum)
-                : launch_defer<1, 1, 16, false, true, true, 4, 1>(H, idx, rows, W, V, d, nullptr, ldo, group_m,
+                : launch_defer<1, 1, 16, false, true, true, 4, true>(H, idx, rows, W, V, d, nullptr, ldo, group_m,
                                                                   stream, pmax, parg, psum);
     else
         e = out ? launch_defer<2, 4, 8, true, true>(H, idx, rows, W, V, d, out, ldo, group_m, stream, pmax, parg, psum)
@@ -1948,11 +1920,11 @@ hipError_t launch_gather_gemm(int variant, const void *H, const int32_t *idx, in
         return out_bf16 ? launch_defer<1, 1, 16, true, false, true>(H, idx, rows, W, V, d, out, ldo, group_m, stream)
                         : hipErrorInvalidValue;
     case kVariantBf16M16Dma4:
-        return out_bf16 ? launch_defer<1, 1, 16, true, false, true, 4, 0>(H, idx, rows, W, V, d, out, ldo, group_m,
+        return out_bf16 ? launch_defer<1, 1, 16, true, false, true, 4, false>(H, idx, rows, W, V, d, out, ldo, group_m,
                                                                          stream)
                         : hipErrorInvalidValue;
     case kVariantBf16M16Dma4W3:
-        return out_bf16 ? launch_defer<1, 1, 16, true, false, true, 4, 1>(H, idx, rows, W, V, d, out, ldo, group_m,
+        return out_bf16 ? launch_defer<1, 1, 16, true, false, true, 4, true>(H, idx, rows, W, V, d, out, ldo, group_m,
                                                                          stream)
                         : hipErrorInvalidValue;
     case kVariantBf16PersistK32:
