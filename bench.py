@@ -48,6 +48,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 LOWM_VARIANTS = (20,)
+DEVICE_COUNT_VARIANT = 22   # the kernel mosaic_masked_logits_device_count runs
 WARMUP_MIN_STEPS = 3
 WARMUP_MIN_SECONDS = 0.15
 
@@ -288,6 +289,10 @@ def main():
     ap.add_argument("--workload", default="long_logits")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--count-on-host", action="store_true",
+                    help="single-launch logits workloads: read the masked count back to the host before "
+                         "the GEMM (mosaic_masked_logits) instead of letting the kernel read it on the device "
+                         "(mosaic_masked_logits_device_count, the default there)")
     ap.add_argument("--profile-copy-mib", type=int, default=0,
                     help="after the timed steps, run a plain elementwise copy of this many MiB three times "
                          "(a kernel of known traffic that calibrates rocprofv3's FETCH_SIZE/WRITE_SIZE)")
@@ -392,6 +397,12 @@ def main():
         variant = mosaic.mosaic_logits_variant(rows_per_launch, V, d, H.dtype, out_dtype)
         log(f"[bench] M={M} chunk_rows={C} launches={launches} variant={variant} "
             f"out={out.numel() * out.element_size() / 1e9:.2f} GB")
+    # One launch on the default persistent kernel: the kernel reads the count the compaction
+    # left in device memory, so the step has no device-to-host read-back (the output buffer
+    # was sized once, from the first count, as a denoising loop whose masked set only
+    # shrinks can do).
+    count_on_device = (args.path == "logits" and launches == 1 and not args.count_on_host and
+                       variant == DEVICE_COUNT_VARIANT)
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -402,10 +413,11 @@ def main():
         if seq_offsets is not None:
             mosaic.mosaic_mask_compact_batched(tokens, seq_offsets, wl.mask_id, idx=idx,
                                                idx_offsets=cnt[: wl.nseq + 1], stream=stream)
-            m = int(cnt[wl.nseq].item())      # device -> host: sizes the GEMM
+            cdev = cnt[wl.nseq: wl.nseq + 1]
         else:
             mosaic.mosaic_mask_compact(tokens, wl.mask_id, idx=idx, count=cnt[:1], stream=stream)
-            m = int(cnt[0].item())
+            cdev = cnt[:1]
+        m = M if count_on_device else int(cdev.item())     # device -> host: sizes the GEMM
         if i is not None:
             ev[i][1].record(stream)
         if consumer:
@@ -418,6 +430,8 @@ def main():
             mosaic.mosaic_masked_logits(H, all_rows, W, M=L, out=full, chunk_rows=C, stream=stream)
             sel.copy_(idx[:m])
             torch.index_select(full, 0, sel, out=out)
+        elif count_on_device:
+            mosaic.mosaic_masked_logits_device_count(H, idx, W, cdev, max_rows=M, out=out, stream=stream)
         else:
             mosaic.mosaic_masked_logits(H, idx, W, M=m, out=out, chunk_rows=C, stream=stream)
         if i is not None:
@@ -432,6 +446,8 @@ def main():
         assert step(i) == M
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if count_on_device:   # the count the kernels read (checked after the timed region)
+        assert int((cnt[wl.nseq] if seq_offsets is not None else cnt[0]).item()) == M
     ms_per_step = wall * 1e3 / args.steps
     gemm_ms = [a[1].elapsed_time(a[2]) for a in ev]
     compact_ms = [a[0].elapsed_time(a[1]) for a in ev]
@@ -495,7 +511,8 @@ def main():
         "config": {"workload": args.workload, "L": L, "d": d, "V": V, "M": M, "chunk_rows": C,
                    "launches_per_step": launches, "in_dtype": wl.dtype,
                    "out_dtype": "per-row f32 max / i32 argmax / f32 lse" if consumer else wl.out_dtype,
-                   "accumulate": "fp32", "path": args.path},
+                   "accumulate": "fp32", "path": args.path,
+                   "count": "device (no read-back)" if count_on_device else "host (read back before the GEMM)"},
         "roofline": roofline,
         "detail": {"gemm_ms_per_step": round(gemm_avg, 4), "gemm_ms_median": round(gemm_median, 4),
                    "gemm_ms_min": round(min(gemm_ms), 4),

@@ -163,6 +163,31 @@ mosaic_status_t mosaic_masked_logits(const void *H, int64_t L, int64_t d,
                                      mosaic_dtype_t in_dtype, mosaic_dtype_t out_dtype,
                                      void *stream);
 
+/* Steps 2 and 3 with the row count read on the device ([MR] 核心组件 1; [MP] §2.2):
+ * as mosaic_masked_logits in one chunk, with M = min(max(*count, 0), max_rows) read by
+ * the kernel when it starts.  count is an int32 in device memory written earlier on the
+ * same stream, for example mosaic_mask_compact's count, so the host neither reads it back
+ * nor waits: the compaction and the logits can be enqueued back to back (and captured in
+ * a graph).  A denoising loop whose masked set only shrinks can size out once, from the
+ * first step's count, and pass that as max_rows afterwards.
+ *   idx       int32[max_rows]      rows of H, as in mosaic_masked_logits; only the
+ *                                  first M are read.
+ *   count     int32* (device)      the number of rows.  Negative values count as 0,
+ *                                  values above max_rows as max_rows: nothing waits for
+ *                                  the value, so no error can be reported for it.
+ *   max_rows  capacity of idx and out in rows; the launch is sized for it.
+ *   out       [max_rows, V]        rows < M get the logits; rows >= M are not written.
+ * Supported: BF16 -> BF16 with d % 64 == 0 (the persistent kernel of the default path,
+ * bit-identical to mosaic_masked_logits), else UNSUPPORTED.  Other requirements and
+ * argument errors as for mosaic_masked_logits; count must be 4-byte aligned.
+ * max_rows == 0 or V == 0: MOSAIC_OK and nothing is enqueued.  The MOSAIC_CHECK_IDX debug
+ * check is not made here (it needs M on the host). */
+mosaic_status_t mosaic_masked_logits_device_count(const void *H, int64_t L, int64_t d,
+                                                  const int32_t *idx, const int32_t *count,
+                                                  int64_t max_rows, const void *W, int64_t V,
+                                                  void *out, mosaic_dtype_t in_dtype,
+                                                  mosaic_dtype_t out_dtype, void *stream);
+
 /* ------------------------------------------------------- per-row consumer --- */
 
 /* The sampler's view of each masked row, reduced inside the logits kernel so a row's

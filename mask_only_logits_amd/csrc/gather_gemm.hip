@@ -764,8 +764,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_pe
 gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__restrict__ idx, int32_t rows,
                               const __bf16 *__restrict__ W, int32_t V, int32_t d, __bf16 *__restrict__ out,
                               int64_t ldo, int32_t group_m, float *__restrict__ pmax,
-                              int32_t *__restrict__ parg, float *__restrict__ psum)
+                              int32_t *__restrict__ parg, float *__restrict__ psum,
+                              const int32_t *__restrict__ rows_dev)
 {
+    // rows_dev: the row count in device memory, written earlier on the stream (the launch
+    // grid was sized for `rows`, the capacity); negative counts are 0, larger ones `rows`
+    if (rows_dev)
+        rows = min(max(*rows_dev, 0), rows);
     constexpr int NW = 8, BV = 256, BM = 256, BK = 64, NSTAGE = 2;
     constexpr int WST = DEEP ? 3 : 2, HST = 2;   // W and H stages
     constexpr int ROW_BYTES = BK * 2;
@@ -1809,7 +1814,7 @@ template <int NSPREAD, int DEFER, int NIMM, bool STORE = true, bool REDUCE = fal
           int DMAW = 8, bool DEEP = false>
 hipError_t launch_defer(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V, int64_t d,
                         void *out, int64_t ldo, int group_m, hipStream_t stream, float *pmax = nullptr,
-                        int32_t *parg = nullptr, float *psum = nullptr)
+                        int32_t *parg = nullptr, float *psum = nullptr, const int32_t *rows_dev = nullptr)
 {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
@@ -1819,7 +1824,7 @@ hipError_t launch_defer(const void *H, const int32_t *idx, int64_t rows, const v
     grid = std::min<int64_t>(grid, ((ntiles + 7) / 8) * 8);
     hipLaunchKernelGGL((gather_gemm_bf16_defer_kernel<NSPREAD, DEFER, NIMM, STORE, REDUCE, M16, DMAW, DEEP>),
                        dim3((unsigned)grid), dim3(512), 0, stream, (const __bf16 *)H, idx, (int32_t)rows, (const __bf16 *)W, (int32_t)V,
-                       (int32_t)d, (__bf16 *)out, ldo, group_m, pmax, parg, psum);
+                       (int32_t)d, (__bf16 *)out, ldo, group_m, pmax, parg, psum, rows_dev);
     return hipGetLastError();
 }
 
@@ -1843,6 +1848,16 @@ hipError_t launch_lowm_shared(const void *H, const int32_t *idx, int64_t rows, c
 }
 
 }  // namespace
+
+hipError_t launch_gather_gemm_device_rows(const void *H, const int32_t *idx, const int32_t *rows_dev,
+                                          int64_t max_rows, const void *W, int64_t V, int64_t d, void *out,
+                                          int64_t ldo, int group_m, hipStream_t stream)
+{
+    if (group_m <= 0)
+        group_m = kDefaultGroupM;
+    return launch_defer<1, 1, 16, true, false, true, 4, true>(H, idx, max_rows, W, V, d, out, ldo, group_m, stream,
+                                                              nullptr, nullptr, nullptr, rows_dev);
+}
 
 bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V)
 {

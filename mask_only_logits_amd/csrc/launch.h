@@ -46,6 +46,13 @@ hipError_t launch_gather_gemm(int variant, const void *H, const int32_t *idx, in
                               const void *W, int64_t V, int64_t d, void *out, int64_t ldo,
                               bool out_bf16, int group_m, hipStream_t stream);
 
+// One launch whose row count is read by the kernel from device memory: rows =
+// clamp(*rows_dev, 0, max_rows) (bf16 -> bf16, d % 64 == 0; the default persistent form,
+// its grid sized for max_rows).
+hipError_t launch_gather_gemm_device_rows(const void *H, const int32_t *idx, const int32_t *rows_dev,
+                                          int64_t max_rows, const void *W, int64_t V, int64_t d, void *out,
+                                          int64_t ldo, int group_m, hipStream_t stream);
+
 // One chunk of the per-row consumer (bf16 in, d % 64 == 0): the persistent kernel
 // reduces every (row, 256-entry vocabulary tile) to a partial in pmax / parg / psum
 // ([ceil(V/256)][rows] each) and, when `out` is not null, also stores the bf16 logits;

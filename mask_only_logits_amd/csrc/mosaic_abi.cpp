@@ -353,6 +353,37 @@ mosaic_status_t mosaic_masked_logits(const void *H, int64_t L, int64_t d, const 
     return MOSAIC_OK;
 }
 
+mosaic_status_t mosaic_masked_logits_device_count(const void *H, int64_t L, int64_t d, const int32_t *idx,
+                                                  const int32_t *count, int64_t max_rows, const void *W, int64_t V,
+                                                  void *out, mosaic_dtype_t in_dtype, mosaic_dtype_t out_dtype,
+                                                  void *stream)
+{
+    if (max_rows < 0 || V < 0 || L < 0 || d < 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    const int64_t in_es = esize_of(in_dtype), out_es = esize_of(out_dtype);
+    if (in_es == 0 || out_es == 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (in_dtype != MOSAIC_BF16 || out_dtype != MOSAIC_BF16 || d % 64 != 0)
+        return MOSAIC_ERR_UNSUPPORTED;
+    if (max_rows == 0 || V == 0)
+        return MOSAIC_OK;
+    if (!H || !W || !idx || !count || !out || L == 0 || d == 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (!aligned16(H) || !aligned16(W) || !aligned16(out) || ((uintptr_t)idx & 3u) || ((uintptr_t)count & 3u))
+        return MOSAIC_ERR_INVALID_ARG;
+    if (checked_bytes(max_rows, V, out_es) < 0 || checked_bytes(L, d, in_es) < 0 ||
+        checked_bytes(V, d, in_es) < 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (L > kMaxPos || V > kMaxPos || d > kMaxPos || max_rows > kMaxPos)
+        return MOSAIC_ERR_UNSUPPORTED;
+    if (!variant_can_run(mosaic::kVariantBf16M16Dma4W3, max_rows, d, in_dtype, out_dtype) ||
+        !mosaic::gather_gemm_grid_fits(mosaic::kVariantBf16M16Dma4W3, max_rows, V))
+        return MOSAIC_ERR_UNSUPPORTED;
+    const hipError_t e = mosaic::launch_gather_gemm_device_rows(H, idx, count, max_rows, W, V, d, out, V,
+                                                                read_tune().group_m, (hipStream_t)stream);
+    return e == hipSuccess ? MOSAIC_OK : MOSAIC_ERR_DEVICE;
+}
+
 mosaic_status_t mosaic_lazy_chunk_rows(int64_t M, int64_t V, mosaic_dtype_t out_dtype, int64_t budget_bytes,
                                       int64_t *chunk_rows, int64_t *num_chunks)
 {

@@ -33,6 +33,7 @@ EXPORTS = (
     "mosaic_mask_compact_flags",
     "mosaic_mask_compact_batched",
     "mosaic_masked_logits",
+    "mosaic_masked_logits_device_count",
     "mosaic_num_chunks",
     "mosaic_logits_bytes",
     "mosaic_logits_variant",
@@ -72,6 +73,8 @@ def _load() -> ctypes.CDLL:
     lib.mosaic_mask_compact_batched.argtypes = [p, i64, p, i32, i32, p, p, p, sz, p]
     lib.mosaic_masked_logits.restype = st
     lib.mosaic_masked_logits.argtypes = [p, i64, i64, p, i64, p, i64, p, i64, st, st, p]
+    lib.mosaic_masked_logits_device_count.restype = st
+    lib.mosaic_masked_logits_device_count.argtypes = [p, i64, i64, p, p, i64, p, i64, p, st, st, p]
     lib.mosaic_num_chunks.restype = i64
     lib.mosaic_num_chunks.argtypes = [i64, i64]
     lib.mosaic_logits_bytes.restype = st
@@ -263,6 +266,33 @@ def mosaic_masked_logits(H: torch.Tensor, idx: torch.Tensor, W: torch.Tensor, M:
     _check(lib.mosaic_masked_logits(_dev(H, "H"), L, d, _dev(idx, "idx", torch.int32), M, _dev(W, "W"), V,
                                     _dev(out, "out"), int(chunk_rows), _dtype_code(H.dtype),
                                     _dtype_code(out.dtype), _stream(stream)), "mosaic_masked_logits")
+    return out
+
+
+def mosaic_masked_logits_device_count(H: torch.Tensor, idx: torch.Tensor, W: torch.Tensor, count: torch.Tensor,
+                                      max_rows: int | None = None, out: torch.Tensor | None = None,
+                                      stream=None) -> torch.Tensor:
+    """logits = H[idx[:M], :] @ W.T with M = clamp(count[0], 0, max_rows) read on the device
+    (count: an int32 device tensor, e.g. mosaic_mask_compact's count); nothing waits for
+    it.  bf16 H [L, d] and W [V, d] with d % 64 == 0.  `out` (allocated if absent) is
+    [max_rows, V] (max_rows defaults to idx.numel()); rows >= M are not written."""
+    if H.dim() != 2 or W.dim() != 2 or H.shape[1] != W.shape[1]:
+        raise ValueError("H must be [L, d] and W [V, d]")
+    if H.dtype != W.dtype:
+        raise TypeError("H and W must share a dtype")
+    L, d = H.shape
+    V = W.shape[0]
+    max_rows = idx.numel() if max_rows is None else int(max_rows)
+    if max_rows > idx.numel():
+        raise ValueError("max_rows exceeds the length of idx")
+    if out is None:
+        out = torch.empty((max_rows, V), dtype=H.dtype, device=H.device)
+    elif out.numel() < max_rows * V:
+        raise ValueError("out is smaller than max_rows * V")
+    _check(lib.mosaic_masked_logits_device_count(_dev(H, "H"), L, d, _dev(idx, "idx", torch.int32),
+                                                 _dev(count, "count", torch.int32), max_rows, _dev(W, "W"), V,
+                                                 _dev(out, "out"), _dtype_code(H.dtype), _dtype_code(out.dtype),
+                                                 _stream(stream)), "mosaic_masked_logits_device_count")
     return out
 
 

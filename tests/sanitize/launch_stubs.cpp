@@ -31,6 +31,11 @@ hipError_t launch_gather_gemm(int, const void *, const int32_t *, int64_t, const
 {
     return hipErrorInvalidValue;
 }
+hipError_t launch_gather_gemm_device_rows(const void *, const int32_t *, const int32_t *, int64_t, const void *,
+                                          int64_t, int64_t, void *, int64_t, int, hipStream_t)
+{
+    return hipErrorInvalidValue;
+}
 hipError_t launch_logits_argmax_lse(const void *, const int32_t *, int64_t, const void *, int64_t, int64_t, void *,
                                     int64_t, float *, int32_t *, float *, float *, int32_t *, float *, int, bool,
                                     hipStream_t)

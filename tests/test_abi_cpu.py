@@ -99,6 +99,30 @@ def test_empty_problems_are_ok_without_pointers(m):
     assert _logits(m, V=0, H=None, W=None, idx=None, out=None) == 0
 
 
+def _logits_dc(m, H=A16, L=100, d=64, idx=A16, count=A16, R=10, W=A16, V=50, out=A16, i=1, o=1):
+    return m.lib.mosaic_masked_logits_device_count(H, L, d, idx, count, R, W, V, out, i, o, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(R=-1), 1), (dict(V=-1), 1), (dict(L=-1), 1), (dict(d=-1), 1),
+    (dict(H=None), 1), (dict(W=None), 1), (dict(idx=None), 1), (dict(out=None), 1), (dict(count=None), 1),
+    (dict(L=0), 1),
+    (dict(H=A8), 1), (dict(W=A8), 1), (dict(out=A8), 1), (dict(idx=A16 + 2), 1), (dict(count=A16 + 2), 1),
+    (dict(i=5), 1), (dict(o=9), 1),
+    # one form only: bf16 -> bf16, d % 64 == 0
+    (dict(d=96), 2), (dict(i=0, o=0), 2), (dict(i=1, o=0), 2), (dict(i=0, o=1), 2),
+    (dict(R=2**40, V=2**30), 1),
+    (dict(L=2**31), 2), (dict(R=2**31), 2),
+])
+def test_logits_device_count_validation(m, kw, status):
+    assert _logits_dc(m, **kw) == status
+
+
+def test_device_count_empty_problems_are_ok_without_pointers(m):
+    assert _logits_dc(m, R=0, H=None, W=None, idx=None, count=None, out=None) == 0
+    assert _logits_dc(m, V=0, H=None, W=None, idx=None, count=None, out=None) == 0
+
+
 def test_compact_workspace_bytes(m):
     f = m.lib.mosaic_mask_compact_workspace_bytes
     for L in (0, 1, 8192, 131072, 2**31 - 1):

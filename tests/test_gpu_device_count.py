@@ -1,0 +1,82 @@
+"""GPU checks of mosaic_masked_logits_device_count: the row count read by the kernel from
+device memory (the compaction's count, with no read-back) gives the same bits as the call
+that takes M from the host, writes no row at or past the count, and clamps the count to
+[0, max_rows]."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mask_only_logits_amd import inputs
+from tests.helpers import assert_close, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+POISON = -12352.0    # exact in bf16
+
+
+@pytest.fixture(scope="module")
+def m():
+    from mask_only_logits_amd import mosaic
+    return mosaic
+
+
+def _poisoned(rows, V):
+    return torch.full((rows, V), POISON, dtype=torch.bfloat16, device=DEV)
+
+
+@pytest.mark.parametrize("L,d,V,M", [(700, 64, 1000, 600), (900, 256, 5000, 700), (3000, 192, 2100, 2600),
+                                     (300, 4096, 300, 1), (17000, 128, 700, 16500)])
+def test_count_from_compaction_equals_host_count(m, L, d, V, M):
+    wl = inputs.make_random(L + d + V, L=L, d=d, V=V, M=M, dtype="bf16")
+    tokens = wl.tokens.to(DEV)
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    idx, cnt = m.mosaic_mask_compact(tokens, wl.mask_id)            # count stays on the device
+    out = _poisoned(L, V)
+    m.mosaic_masked_logits_device_count(H, idx, W, cnt, max_rows=L, out=out)
+    Mh = int(cnt.item())
+    ref = m.mosaic_masked_logits(H, idx, W, M=Mh)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:Mh], ref)
+    assert bool((out[Mh:].float() == POISON).all())                 # rows past the count untouched
+    want = oracle.mask_compact(wl.tokens, wl.mask_id)
+    rows = sample_rows(Mh, 0, 12)
+    assert_close(out[torch.as_tensor(rows, device=DEV)], oracle.masked_logits(wl.H, want[rows], wl.W), "devcount")
+
+
+def test_count_is_clamped(m):
+    wl = inputs.make_random(5, L=800, d=128, V=900, M=600, dtype="bf16")
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    idx = torch.from_numpy(oracle.mask_compact(wl.tokens, wl.mask_id)).to(DEV)
+    full = m.mosaic_masked_logits(H, idx, W)
+    for c, rows in ((0, 0), (-5, 0), (1, 1), (300, 300), (500, 500), (600, 500), (10**6, 500)):
+        out = _poisoned(500, wl.V)
+        cnt = torch.tensor([c], dtype=torch.int32, device=DEV)
+        m.mosaic_masked_logits_device_count(H, idx[:500], W, cnt, max_rows=500, out=out)
+        torch.cuda.synchronize()
+        assert torch.equal(out[:rows], full[:rows]), c
+        assert bool((out[rows:].float() == POISON).all()), c
+
+
+def test_llada_step_back_to_back(m):
+    # the LLaDA-shaped step with no host read of the count: compaction then logits
+    wl = inputs.make_workload("llada_step")
+    tokens = wl.tokens.to(DEV)
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    idx, cnt = m.mosaic_mask_compact(tokens, wl.mask_id)
+    M = int(cnt.item())
+    out = _poisoned(M, wl.V)
+    for _ in range(3):                                               # repeated steps, same buffers
+        m.mosaic_mask_compact(tokens, wl.mask_id, idx=idx, count=cnt)
+        m.mosaic_masked_logits_device_count(H, idx, W, cnt, max_rows=M, out=out)
+    ref = m.mosaic_masked_logits(H, idx, W, M=M)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_rejects_other_dtypes(m):
+    wl = inputs.make_random(6, L=100, d=64, V=50, M=10, dtype="f32")
+    idx = torch.arange(10, dtype=torch.int32, device=DEV)
+    cnt = torch.tensor([10], dtype=torch.int32, device=DEV)
+    with pytest.raises(m.MosaicError):
+        m.mosaic_masked_logits_device_count(wl.H.to(DEV), idx, wl.W.to(DEV), cnt)
