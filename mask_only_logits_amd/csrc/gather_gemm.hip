@@ -23,11 +23,13 @@
 //    per phase at the same logical chunk) hit distinct banks.
 //  * K pipeline: NSTAGE LDS buffers.  A stage is refilled as soon as the barrier of
 //    the step that used it has passed, with explicit vmcnt waits and a bare s_barrier
-//    (no full fence), while MFMAs of the last k sub-step run.
+//    (no full fence), while MFMAs of the last k sub-step run.  The default bf16-output
+//    kernel has only waves 0-3 (one per SIMD) request K tiles and gives W a third stage.
 //  * Block mapping: the hardware deals consecutive workgroups round-robin to the 8
 //    XCDs.  Workgroup ids are renumbered so each XCD works on a contiguous range of
 //    tiles, ordered so that groups of GROUP_M row-tiles share one W slab in that XCD's
-//    L2.
+//    L2; on large launches the persistent kernel sets the eight XCDs side by side over
+//    the vocabulary instead.
 //  * Bit-identity across chunks: every output element is one accumulation chain over
 //    k in ascending order in the same MFMA positions whatever the chunk, tile or row
 //    position, so splitting the rows into chunks never changes a bit.  (The two MFMA
@@ -1411,10 +1413,10 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
             zero_acc();
         }
         load_hidx(i + 2);
-        if constexpr (REDUCE) {
-            // red_lds is rewritten at the next tile's end; its readers finish first
-            // (that tile's K loop has barriers), so no extra barrier is needed here.
-        }
+        // (REDUCE: red_lds is next written at the next tile's end, and with RED_IN_STAGE its
+        // stage is next refilled by the next tile's first step; both come after that tile's
+        // first barrier, which every reader of the partials has passed, so no extra barrier
+        // is needed here.)
     }
     };
     if (DMAW < 8 && !dma_wave)
