@@ -59,6 +59,20 @@ int main()
     EXPECT(mosaic_masked_logits(H, 100, 64, idx, 0, W, 10, nullptr, 0, MOSAIC_BF16, MOSAIC_BF16, nullptr) == 0);
     EXPECT(mosaic_masked_logits(H, (int64_t)1 << 31, 64, idx, 10, W, 10, A16, 0, MOSAIC_BF16, MOSAIC_BF16,
                                 nullptr) == 2);
+    // the device-count entry point: validation only (the count is never read on the host)
+    const int32_t *cnt = (const int32_t *)A16;
+    EXPECT(mosaic_masked_logits_device_count(H, 100, 64, idx, cnt, big, W, big, A16, MOSAIC_BF16, MOSAIC_BF16,
+                                             nullptr) == 1);
+    EXPECT(mosaic_masked_logits_device_count(H, 100, 96, idx, cnt, 10, W, 10, A16, MOSAIC_BF16, MOSAIC_BF16,
+                                             nullptr) == 2);
+    EXPECT(mosaic_masked_logits_device_count(H, 100, 64, idx, nullptr, 10, W, 10, A16, MOSAIC_BF16, MOSAIC_BF16,
+                                             nullptr) == 1);
+    EXPECT(mosaic_masked_logits_device_count(H, 100, 64, idx, cnt, 0, W, 10, nullptr, MOSAIC_BF16, MOSAIC_BF16,
+                                             nullptr) == 0);
+    EXPECT(mosaic_masked_logits_device_count(H, 100, 64, idx, cnt, (int64_t)1 << 31, W, 10, A16, MOSAIC_BF16,
+                                             MOSAIC_BF16, nullptr) == 2);
+    EXPECT(mosaic_masked_logits_device_count(H, 100, 64, idx, cnt, 10, W, 10, A16, (mosaic_dtype_t)7, MOSAIC_BF16,
+                                             nullptr) == 1);
     float *f = (float *)A16;
     int32_t *ia = (int32_t *)A16;
     EXPECT(mosaic_masked_logits_argmax_lse(H, 100, 64, idx, 10, W, 50, nullptr, 0, MOSAIC_BF16, MOSAIC_BF16, f, ia,
