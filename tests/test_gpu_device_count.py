@@ -80,3 +80,43 @@ def test_rejects_other_dtypes(m):
     cnt = torch.tensor([10], dtype=torch.int32, device=DEV)
     with pytest.raises(m.MosaicError):
         m.mosaic_masked_logits_device_count(wl.H.to(DEV), idx, wl.W.to(DEV), cnt)
+
+
+def test_compaction_and_logits_in_one_graph(m):
+    # With the count read on the device, a step (compaction, then logits) has no host sync
+    # and can be captured once and replayed; the mask changes between replays (eager work
+    # and synchronisation in between), and every replay matches the eager calls.
+    L, d, V = 3000, 256, 2000
+    wl = inputs.make_random(91, L=L, d=d, V=V, M=2000, dtype="bf16")
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    tokens = wl.tokens.to(DEV).clone()
+    idx = torch.empty(L, dtype=torch.int32, device=DEV)
+    cnt = torch.empty(1, dtype=torch.int32, device=DEV)
+    out = _poisoned(L, V)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                                     # eager run on the capture stream
+        m.mosaic_mask_compact(tokens, wl.mask_id, idx=idx, count=cnt)
+        m.mosaic_masked_logits_device_count(H, idx, W, cnt, max_rows=L, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.mosaic_mask_compact(tokens, wl.mask_id, idx=idx, count=cnt)
+        m.mosaic_masked_logits_device_count(H, idx, W, cnt, max_rows=L, out=out)
+    rng = np.random.default_rng(7)
+    for ratio in (0.9, 0.3, 0.0, 0.65):
+        t = rng.integers(0, wl.mask_id, size=L).astype(np.int32)
+        t[rng.random(L) < ratio] = wl.mask_id
+        tokens.copy_(torch.from_numpy(t).to(DEV))
+        out.fill_(POISON)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = oracle.mask_compact(torch.from_numpy(t), wl.mask_id)
+        M = int(cnt.item())
+        assert M == want.size
+        ref = m.mosaic_masked_logits(H, torch.from_numpy(want).to(DEV), W, M=M) if M else out[:0]
+        torch.cuda.synchronize()
+        assert torch.equal(out[:M], ref), ratio
+        assert bool((out[M:].float() == POISON).all()), ratio
