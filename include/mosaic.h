@@ -223,6 +223,26 @@ mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_
                                                 void *workspace, int64_t workspace_bytes,
                                                 void *stream);
 
+/* The per-row consumer with the row count read on the device, as
+ * mosaic_masked_logits_device_count is to mosaic_masked_logits: one chunk, M =
+ * min(max(*count, 0), max_rows) read by the kernels when they start, so a sampling step
+ * (compaction, then the per-row reductions) needs no read-back and no host wait.
+ *   count      int32* (device); values outside [0, max_rows] are clamped (no error can be
+ *              reported: nothing waits for the value).
+ *   max_rows   capacity of idx, out (if given), row_max, row_argmax and row_lse in rows.
+ *   workspace  at least mosaic_logits_argmax_lse_workspace_bytes(max_rows, 0, V) bytes.
+ * Rows >= M of out, row_max, row_argmax and row_lse are not written.  Other arguments,
+ * requirements and errors as for mosaic_masked_logits_argmax_lse (count 4-byte aligned);
+ * max_rows == 0: MOSAIC_OK, nothing enqueued.  The MOSAIC_CHECK_IDX check is not made. */
+mosaic_status_t mosaic_masked_logits_argmax_lse_device_count(const void *H, int64_t L, int64_t d,
+                                                             const int32_t *idx, const int32_t *count,
+                                                             int64_t max_rows, const void *W, int64_t V,
+                                                             void *out, mosaic_dtype_t in_dtype,
+                                                             mosaic_dtype_t out_dtype, float *row_max,
+                                                             int32_t *row_argmax, float *row_lse,
+                                                             void *workspace, int64_t workspace_bytes,
+                                                             void *stream);
+
 /* Size of the library-owned device array behind mosaic_masked_logits_argmax_lse_noalloc
  * (32 MiB; each device that runs the call holds one until the process ends). */
 #define MOSAIC_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)

@@ -770,7 +770,9 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
                               const int32_t *__restrict__ rows_dev)
 {
     // rows_dev: the row count in device memory, written earlier on the stream (the launch
-    // grid was sized for `rows`, the capacity); negative counts are 0, larger ones `rows`
+    // grid was sized for `rows`, the capacity); negative counts are 0, larger ones `rows`.
+    // The REDUCE partials keep the capacity as their row stride.
+    const int32_t ldp = rows;
     if (rows_dev)
         rows = min(max(*rows_dev, 0), rows);
     constexpr int NW = 8, BV = 256, BM = 256, BK = 64, NSTAGE = 2;
@@ -1219,7 +1221,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     auto reduce_part2 = [&](int m0, int v0) __attribute__((always_inline)) {
         if (wv != 0 || !row_owner)
             return;
-        const int64_t col = (int64_t)(v0 / BV) * rows;
+        const int64_t col = (int64_t)(v0 / BV) * ldp;
 #pragma unroll
         for (int bm = 0; bm < AM; ++bm) {
             const int r = wm * WM + bm * MB + row_lane;
@@ -1451,8 +1453,12 @@ __global__ __launch_bounds__(1024) void logits_reduce_finish_kernel(const float 
                                                                    const float *__restrict__ psum, int32_t ncol,
                                                                    int32_t rows, float *__restrict__ row_max,
                                                                    int32_t *__restrict__ row_argmax,
-                                                                   float *__restrict__ row_lse)
+                                                                   float *__restrict__ row_lse,
+                                                                   const int32_t *__restrict__ rows_dev)
 {
+    // rows: the partials' row stride (the launch's capacity); rows_dev, if set, the count of
+    // rows to finish, read from device memory and clamped to [0, rows]
+    const int nrows = rows_dev ? min(max(*rows_dev, 0), rows) : rows;
     constexpr int NWF = 16;
     constexpr float kLn2 = 0.6931471805599453f;
     __shared__ float sm_m[NWF][64], sm_s[NWF][64];
@@ -1462,7 +1468,7 @@ __global__ __launch_bounds__(1024) void logits_reduce_finish_kernel(const float 
     const int c0 = (int)((int64_t)ncol * w / NWF), c1 = (int)((int64_t)ncol * (w + 1) / NWF);
     float m = -INFINITY, s = 0.0f;
     int a = INT32_MAX;
-    if (r < rows) {
+    if (r < nrows) {
         int c = c0;
         for (; c + 4 <= c1; c += 4) {
             float x[4], sx[4];
@@ -1487,7 +1493,7 @@ __global__ __launch_bounds__(1024) void logits_reduce_finish_kernel(const float 
     sm_a[w][lane] = a;
     sm_s[w][lane] = s;
     __syncthreads();
-    if (w == 0 && r < rows) {
+    if (w == 0 && r < nrows) {
         float mm = -INFINITY, ss = 0.0f;
         int aa = INT32_MAX;
         for (int k = 0; k < NWF; ++k)
@@ -1884,25 +1890,26 @@ bool gather_gemm_grid_fits(int variant, int64_t rows, int64_t V)
 hipError_t launch_logits_argmax_lse(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V,
                                     int64_t d, void *out, int64_t ldo, float *pmax, int32_t *parg, float *psum,
                                     float *row_max, int32_t *row_argmax, float *row_lse, int group_m,
-                                    bool m16, hipStream_t stream)
+                                    bool m16, hipStream_t stream, const int32_t *rows_dev)
 {
     if (group_m <= 0)
         group_m = kDefaultGroupM;
     hipError_t e;
     if (m16)
         e = out ? launch_defer<1, 1, 16, true, true, true, 4, true>(H, idx, rows, W, V, d, out, ldo, group_m,
-                                                                 stream, pmax, parg, psum)
+                                                                 stream, pmax, parg, psum, rows_dev)
                 : launch_defer<1, 1, 16, false, true, true, 4, true>(H, idx, rows, W, V, d, nullptr, ldo, group_m,
-                                                                  stream, pmax, parg, psum);
+                                                                  stream, pmax, parg, psum, rows_dev);
     else
-        e = out ? launch_defer<2, 4, 8, true, true>(H, idx, rows, W, V, d, out, ldo, group_m, stream, pmax, parg, psum)
+        e = out ? launch_defer<2, 4, 8, true, true>(H, idx, rows, W, V, d, out, ldo, group_m, stream, pmax, parg, psum,
+                                                    rows_dev)
                 : launch_defer<2, 4, 8, false, true>(H, idx, rows, W, V, d, nullptr, ldo, group_m, stream, pmax, parg,
-                                                     psum);
+                                                     psum, rows_dev);
     if (e != hipSuccess)
         return e;
     const int ncol = (int)((V + 255) / 256);
     hipLaunchKernelGGL(logits_reduce_finish_kernel, dim3((unsigned)((rows + 63) / 64)), dim3(1024), 0, stream, pmax,
-                       parg, psum, ncol, (int32_t)rows, row_max, row_argmax, row_lse);
+                       parg, psum, ncol, (int32_t)rows, row_max, row_argmax, row_lse, rows_dev);
     return hipGetLastError();
 }
 

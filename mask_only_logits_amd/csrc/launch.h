@@ -56,13 +56,15 @@ hipError_t launch_gather_gemm_device_rows(const void *H, const int32_t *idx, con
 // One chunk of the per-row consumer (bf16 in, d % 64 == 0): the persistent kernel
 // reduces every (row, 256-entry vocabulary tile) to a partial in pmax / parg / psum
 // ([ceil(V/256)][rows] each) and, when `out` is not null, also stores the bf16 logits;
-// a finish kernel combines the partials into row_max / row_argmax / row_lse.  m16 selects
+// a finish kernel combines the partials into row_max / row_argmax / row_lse.  With rows_dev,
+// both kernels take clamp(*rows_dev, 0, rows) rows from device memory (rows is then the
+// capacity: the grids and the partials' row stride).  m16 selects
 // the 16 x 16 x 32 MFMA form of the kernel (else 32 x 32 x 16); the two give the same
 // logits, maxima and argmax, and exp sums added in different orders.
 hipError_t launch_logits_argmax_lse(const void *H, const int32_t *idx, int64_t rows, const void *W, int64_t V,
                                     int64_t d, void *out, int64_t ldo, float *pmax, int32_t *parg, float *psum,
                                     float *row_max, int32_t *row_argmax, float *row_lse, int group_m,
-                                    bool m16, hipStream_t stream);
+                                    bool m16, hipStream_t stream, const int32_t *rows_dev = nullptr);
 
 // FP8 LM head.  Quantize `rows` rows of X ([*, d], bf16 or fp32, d % 8 == 0; row r is
 // source row row_idx[r], or r when row_idx is null) to E4M3 codes q ([rows, d]) and

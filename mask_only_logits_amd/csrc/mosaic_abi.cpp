@@ -509,6 +509,51 @@ static mosaic_status_t argmax_lse_impl(const void *H, int64_t L, int64_t d, cons
     return MOSAIC_OK;
 }
 
+mosaic_status_t mosaic_masked_logits_argmax_lse_device_count(const void *H, int64_t L, int64_t d, const int32_t *idx,
+                                                             const int32_t *count, int64_t max_rows, const void *W,
+                                                             int64_t V, void *out, mosaic_dtype_t in_dtype,
+                                                             mosaic_dtype_t out_dtype, float *row_max,
+                                                             int32_t *row_argmax, float *row_lse, void *workspace,
+                                                             int64_t workspace_bytes, void *stream)
+{
+    if (max_rows < 0 || V < 0 || L < 0 || d < 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (esize_of(in_dtype) == 0 || (out && esize_of(out_dtype) == 0))
+        return MOSAIC_ERR_INVALID_ARG;
+    if (max_rows == 0)
+        return MOSAIC_OK;
+    if (V == 0)
+        return MOSAIC_ERR_INVALID_ARG;   // the maximum of an empty row does not exist
+    if (in_dtype != MOSAIC_BF16 || (out && out_dtype != MOSAIC_BF16))
+        return MOSAIC_ERR_UNSUPPORTED;
+    if (d % 64 != 0 || d > (1 << 22))
+        return MOSAIC_ERR_UNSUPPORTED;
+    if (!H || !W || !idx || !count || !row_max || !row_argmax || !row_lse || !workspace || L == 0 || d == 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (!aligned16(H) || !aligned16(W) || (out && !aligned16(out)) || !aligned16(workspace) ||
+        ((uintptr_t)idx & 3u) || ((uintptr_t)count & 3u) || ((uintptr_t)row_max & 3u) ||
+        ((uintptr_t)row_argmax & 3u) || ((uintptr_t)row_lse & 3u))
+        return MOSAIC_ERR_INVALID_ARG;
+    if ((out && checked_bytes(max_rows, V, 2) < 0) || checked_bytes(L, d, 2) < 0 || checked_bytes(V, d, 2) < 0)
+        return MOSAIC_ERR_INVALID_ARG;
+    if (L > kMaxPos || V > kMaxPos || d > kMaxPos || max_rows > kMaxPos ||
+        !mosaic::gather_gemm_grid_fits(mosaic::kVariantBf16DeferS4I8, max_rows, V))
+        return MOSAIC_ERR_UNSUPPORTED;
+    const int64_t need = argmax_lse_partials_bytes(max_rows, V);
+    if (need < 0 || workspace_bytes < need)
+        return MOSAIC_ERR_INVALID_ARG;
+    const int64_t plane = ceil_div(V, 256) * max_rows;
+    float *pmax = (float *)workspace;
+    int32_t *parg = (int32_t *)(pmax + plane);
+    float *psum = (float *)(parg + plane);
+    const Tune t = read_tune();
+    const bool m16 = t.variant != mosaic::kVariantBf16DeferS4I8;
+    const hipError_t e = mosaic::launch_logits_argmax_lse(H, idx, max_rows, W, V, d, out, V, pmax, parg, psum,
+                                                          row_max, row_argmax, row_lse, t.group_m, m16,
+                                                          (hipStream_t)stream, count);
+    return e == hipSuccess ? MOSAIC_OK : MOSAIC_ERR_DEVICE;
+}
+
 mosaic_status_t mosaic_masked_logits_argmax_lse(const void *H, int64_t L, int64_t d, const int32_t *idx, int64_t M,
                                                 const void *W, int64_t V, void *out, int64_t chunk_rows,
                                                 mosaic_dtype_t in_dtype, mosaic_dtype_t out_dtype, float *row_max,

@@ -39,6 +39,7 @@ EXPORTS = (
     "mosaic_logits_variant",
     "mosaic_masked_logits_argmax_lse",
     "mosaic_masked_logits_argmax_lse_noalloc",
+    "mosaic_masked_logits_argmax_lse_device_count",
     "mosaic_logits_argmax_lse_workspace_bytes",
     "mosaic_lazy_chunk_rows",
     "mosaic_quantize_rows_fp8",
@@ -83,6 +84,9 @@ def _load() -> ctypes.CDLL:
     lib.mosaic_logits_variant.argtypes = [i64, i64, i64, st, st]
     lib.mosaic_masked_logits_argmax_lse.restype = st
     lib.mosaic_masked_logits_argmax_lse.argtypes = [p, i64, i64, p, i64, p, i64, p, i64, st, st, p, p, p, p, i64, p]
+    lib.mosaic_masked_logits_argmax_lse_device_count.restype = st
+    lib.mosaic_masked_logits_argmax_lse_device_count.argtypes = [p, i64, i64, p, p, i64, p, i64, p, st, st, p, p, p,
+                                                                 p, i64, p]
     lib.mosaic_masked_logits_argmax_lse_noalloc.restype = st
     lib.mosaic_masked_logits_argmax_lse_noalloc.argtypes = [p, i64, i64, p, i64, p, i64, p, i64, st, st, p, p, p, p]
     lib.mosaic_logits_argmax_lse_workspace_bytes.restype = i64
@@ -345,6 +349,47 @@ def mosaic_masked_logits_argmax_lse(H: torch.Tensor, idx: torch.Tensor, W: torch
         _dev(row_max, "row_max", torch.float32), _dev(row_argmax, "row_argmax", torch.int32),
         _dev(row_lse, "row_lse", torch.float32), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         _stream(stream)), "mosaic_masked_logits_argmax_lse")
+    return row_max, row_argmax, row_lse, out
+
+
+def mosaic_masked_logits_argmax_lse_device_count(H: torch.Tensor, idx: torch.Tensor, W: torch.Tensor,
+                                                 count: torch.Tensor, max_rows: int | None = None,
+                                                 store_logits: bool = False, out: torch.Tensor | None = None,
+                                                 row_max: torch.Tensor | None = None,
+                                                 row_argmax: torch.Tensor | None = None,
+                                                 row_lse: torch.Tensor | None = None,
+                                                 workspace: torch.Tensor | None = None, stream=None):
+    """mosaic_masked_logits_argmax_lse with M = clamp(count[0], 0, max_rows) read on the
+    device (count: an int32 device tensor, e.g. the compaction's count); nothing waits for
+    it.  Arrays are sized for max_rows (default idx.numel()); rows >= M are not written."""
+    if H.dim() != 2 or W.dim() != 2 or H.shape[1] != W.shape[1]:
+        raise ValueError("H must be [L, d] and W [V, d]")
+    L, d = H.shape
+    V = W.shape[0]
+    R = idx.numel() if max_rows is None else int(max_rows)
+    if R > idx.numel():
+        raise ValueError("max_rows exceeds the length of idx")
+    dev = H.device
+    if store_logits and out is None:
+        out = torch.empty((R, V), dtype=torch.bfloat16, device=dev)
+    if out is not None and out.numel() < R * V:
+        raise ValueError("out is smaller than max_rows * V")
+    row_max = torch.empty(R, dtype=torch.float32, device=dev) if row_max is None else row_max
+    row_argmax = torch.empty(R, dtype=torch.int32, device=dev) if row_argmax is None else row_argmax
+    row_lse = torch.empty(R, dtype=torch.float32, device=dev) if row_lse is None else row_lse
+    for name, t in (("row_max", row_max), ("row_argmax", row_argmax), ("row_lse", row_lse)):
+        if t.numel() < R:
+            raise ValueError(f"{name} has fewer than max_rows entries")
+    need = mosaic_logits_argmax_lse_workspace_bytes(R, 0, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(lib.mosaic_masked_logits_argmax_lse_device_count(
+        _dev(H, "H"), L, d, _dev(idx, "idx", torch.int32), _dev(count, "count", torch.int32), R, _dev(W, "W"), V,
+        _dev(out, "out") if out is not None else None, _dtype_code(H.dtype),
+        _dtype_code(out.dtype) if out is not None else MOSAIC_BF16,
+        _dev(row_max, "row_max", torch.float32), _dev(row_argmax, "row_argmax", torch.int32),
+        _dev(row_lse, "row_lse", torch.float32), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(stream)), "mosaic_masked_logits_argmax_lse_device_count")
     return row_max, row_argmax, row_lse, out
 
 

@@ -38,7 +38,7 @@ hipError_t launch_gather_gemm_device_rows(const void *, const int32_t *, const i
 }
 hipError_t launch_logits_argmax_lse(const void *, const int32_t *, int64_t, const void *, int64_t, int64_t, void *,
                                     int64_t, float *, int32_t *, float *, float *, int32_t *, float *, int, bool,
-                                    hipStream_t)
+                                    hipStream_t, const int32_t *)
 {
     return hipErrorInvalidValue;
 }

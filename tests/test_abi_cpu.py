@@ -123,6 +123,27 @@ def test_device_count_empty_problems_are_ok_without_pointers(m):
     assert _logits_dc(m, V=0, H=None, W=None, idx=None, count=None, out=None) == 0
 
 
+def _lse_dc(m, H=A16, L=100, d=64, idx=A16, count=A16, R=10, W=A16, V=50, out=None, i=1, o=1, rm=A16, ra=A16,
+            rl=A16, ws=A16, wsb=1 << 20):
+    return m.lib.mosaic_masked_logits_argmax_lse_device_count(H, L, d, idx, count, R, W, V, out, i, o, rm, ra, rl,
+                                                              ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(R=-1), 1), (dict(V=0), 1), (dict(count=None), 1), (dict(count=A16 + 2), 1), (dict(ws=None), 1),
+    (dict(wsb=16), 1), (dict(rm=None), 1), (dict(rl=A16 + 2), 1), (dict(out=A8), 1),
+    (dict(d=96), 2), (dict(i=0), 2), (dict(out=A16, o=0), 2), (dict(R=2**31), 2),
+])
+def test_argmax_lse_device_count_validation(m, kw, status):
+    assert _lse_dc(m, **kw) == status
+
+
+def test_argmax_lse_device_count_workspace_exact(m):
+    need = m.mosaic_logits_argmax_lse_workspace_bytes(10, 0, 50)
+    assert _lse_dc(m, wsb=need - 1) == 1
+    assert _lse_dc(m, R=0, H=None, W=None, idx=None, count=None, rm=None, ra=None, rl=None, ws=None) == 0
+
+
 def test_compact_workspace_bytes(m):
     f = m.lib.mosaic_mask_compact_workspace_bytes
     for L in (0, 1, 8192, 131072, 2**31 - 1):

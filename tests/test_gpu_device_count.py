@@ -1,7 +1,8 @@
-"""GPU checks of mosaic_masked_logits_device_count: the row count read by the kernel from
-device memory (the compaction's count, with no read-back) gives the same bits as the call
-that takes M from the host, writes no row at or past the count, and clamps the count to
-[0, max_rows]."""
+"""GPU checks of mosaic_masked_logits_device_count and
+mosaic_masked_logits_argmax_lse_device_count: the row count read by the kernels from device
+memory (the compaction's count, with no read-back) gives the same bits as the calls that
+take M from the host (which the oracle parity tests cover), writes no row at or past the
+count, and clamps the count to [0, max_rows]."""
 import numpy as np
 import pytest
 import torch
@@ -120,3 +121,40 @@ def test_compaction_and_logits_in_one_graph(m):
         torch.cuda.synchronize()
         assert torch.equal(out[:M], ref), ratio
         assert bool((out[M:].float() == POISON).all()), ratio
+
+
+@pytest.mark.parametrize("L,d,V,store", [(900, 256, 5000, False), (3000, 192, 2100, True), (700, 64, 300, False),
+                                         (17000, 128, 700, False)])
+def test_consumer_count_from_compaction_equals_host_count(m, L, d, V, store):
+    wl = inputs.make_random(L + d + V + 3, L=L, d=d, V=V, M=int(L * 0.7), dtype="bf16")
+    tokens = wl.tokens.to(DEV)
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    idx, cnt = m.mosaic_mask_compact(tokens, wl.mask_id)
+    sent = (torch.full((L,), -3.0, device=DEV), torch.full((L,), -7, dtype=torch.int32, device=DEV),
+            torch.full((L,), -5.0, device=DEV))
+    out = _poisoned(L, V) if store else None
+    rm, ra, rl, _ = m.mosaic_masked_logits_argmax_lse_device_count(H, idx, W, cnt, max_rows=L, out=out,
+                                                                   row_max=sent[0], row_argmax=sent[1],
+                                                                   row_lse=sent[2])
+    M = int(cnt.item())
+    hm, ha, hl, hout = m.mosaic_masked_logits_argmax_lse(H, idx, W, M=M, store_logits=store)
+    torch.cuda.synchronize()
+    assert torch.equal(rm[:M], hm) and torch.equal(ra[:M], ha) and torch.equal(rl[:M], hl)
+    assert bool((rm[M:] == -3.0).all()) and bool((ra[M:] == -7).all()) and bool((rl[M:] == -5.0).all())
+    if store:
+        assert torch.equal(out[:M], hout) and bool((out[M:].float() == POISON).all())
+    assert M == oracle.mask_compact(wl.tokens, wl.mask_id).size
+
+
+def test_consumer_count_is_clamped(m):
+    wl = inputs.make_random(17, L=800, d=128, V=900, M=600, dtype="bf16")
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    idx = torch.from_numpy(oracle.mask_compact(wl.tokens, wl.mask_id)).to(DEV)
+    fm, fa, fl, _ = m.mosaic_masked_logits_argmax_lse(H, idx[:500], W)
+    for c, rows in ((0, 0), (-1, 0), (1, 1), (499, 499), (777, 500)):
+        cnt = torch.tensor([c], dtype=torch.int32, device=DEV)
+        ra = torch.full((500,), -7, dtype=torch.int32, device=DEV)
+        _, ra, _, _ = m.mosaic_masked_logits_argmax_lse_device_count(H, idx[:500], W, cnt, max_rows=500, row_argmax=ra)
+        torch.cuda.synchronize()
+        assert torch.equal(ra[:rows], fa[:rows]), c
+        assert bool((ra[rows:] == -7).all()), c
