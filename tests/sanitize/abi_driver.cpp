@@ -75,6 +75,14 @@ int main()
                                              nullptr) == 1);
     float *f = (float *)A16;
     int32_t *ia = (int32_t *)A16;
+    EXPECT(mosaic_masked_logits_argmax_lse_device_count(H, 100, 64, idx, cnt, 10, W, 50, nullptr, MOSAIC_BF16,
+                                                        MOSAIC_BF16, f, ia, f, A16, 16, nullptr) == 1);   // short
+    EXPECT(mosaic_masked_logits_argmax_lse_device_count(H, 100, 64, idx, nullptr, 10, W, 50, nullptr, MOSAIC_BF16,
+                                                        MOSAIC_BF16, f, ia, f, A16, 1 << 20, nullptr) == 1);
+    EXPECT(mosaic_masked_logits_argmax_lse_device_count(H, 100, 96, idx, cnt, 10, W, 50, nullptr, MOSAIC_BF16,
+                                                        MOSAIC_BF16, f, ia, f, A16, 1 << 20, nullptr) == 2);
+    EXPECT(mosaic_masked_logits_argmax_lse_device_count(H, 100, 64, idx, cnt, big, W, big, nullptr, MOSAIC_BF16,
+                                                        MOSAIC_BF16, f, ia, f, A16, big, nullptr) == 1);   // overflow
     EXPECT(mosaic_masked_logits_argmax_lse(H, 100, 64, idx, 10, W, 50, nullptr, 0, MOSAIC_BF16, MOSAIC_BF16, f, ia,
                                            f, A16, 10, nullptr) == 1);   // workspace short
     EXPECT(mosaic_masked_logits_argmax_lse(H, 100, 64, idx, big, W, big, nullptr, big, MOSAIC_BF16, MOSAIC_BF16, f,
