@@ -1114,11 +1114,11 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
                     pk[j][3] = s1[1];
                 }
             // Block pairs 2q and 2q + 1 of a row hold its two 64-byte halves of one 128-byte
-            // line.  Lanes r16 and r16 ^ 8 trade words (DPP row rotate by 8) so that one
-            // store instruction writes whole lines: rows 0-7 of the row block (upper lanes
-            // the second halves), then rows 8-15 (lower lanes the first halves).  A
+            // line.  Lanes r16 and r16 ^ 8 trade words so that one store instruction writes
+            // whole lines: rows 0-7 of the row block (upper lanes the second halves), then
+            // rows 8-15 (lower lanes the first halves).  Each is one DPP move (row rotate by
+            // 8) whose bank mask writes only the receiving half of each 16-lane row.  A
             // store-only probe of the two layouts ran at 4.5 and 5.45 TB/s.
-            const bool lo8 = r16 < 8;
 #pragma unroll
             for (int q = 0; q < AV / 4; ++q)
 #pragma unroll
@@ -1126,11 +1126,9 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
                     const int j0 = 2 * q * AM + bm, j1 = j0 + AM;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const uint32_t t = lo8 ? pk[j1][e] : pk[j0][e];
-                        const uint32_t u = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t, 0x128, 0xf, 0xf, false);
-                        const uint32_t x = lo8 ? pk[j0][e] : u, y = lo8 ? u : pk[j1][e];
-                        pk[j0][e] = x;
-                        pk[j1][e] = y;
+                        const int w0 = (int)pk[j0][e], w1 = (int)pk[j1][e];
+                        pk[j0][e] = (uint32_t)__builtin_amdgcn_update_dpp(w0, w1, 0x128, 0xf, 0xc, false);
+                        pk[j1][e] = (uint32_t)__builtin_amdgcn_update_dpp(w1, w0, 0x128, 0xf, 0x3, false);
                     }
                 }
         } else {
