@@ -1394,26 +1394,31 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
         }
         if constexpr (REDUCE)
             reduce_part1(cv0);
-        wait_vmcnt<63>();
-        barrier_no_fence();
         if constexpr (STORE && !REDUCE && NIMM == NST) {
             // Every store of the tile, then the row ids two tiles ahead, then the next tile's
             // first requests: vmcnt drains in issue order, so the next tile's first wait then
             // leaves exactly its later K tiles in flight instead of also waiting for them
-            // behind these stores (+2.5% on a 21399-row launch, neutral on 3687 rows).
-            if (i + 1 < n_my)
-                make_src(i + 1);
+            // behind these stores (+2.5% on a 21399-row launch, neutral on 3687 rows).  All of
+            // it but the requests touches no LDS, so it comes before the tile-end barrier
+            // (which only guards the stages against the next tile's requests): a wave packs
+            // and stores while the other waves finish their last MFMAs.
             pm0 = cm0;
             pv0 = cv0;
             pack();
 #pragma unroll
             for (int j = 0; j < NST; ++j)
                 store_one(j);
+            if (i + 1 < n_my)
+                make_src(i + 1);
             load_hidx(i + 2);
+            wait_vmcnt<63>();
+            barrier_no_fence();
             if (i + 1 < n_my)
                 prologue_t();
             continue;
         }
+        wait_vmcnt<63>();
+        barrier_no_fence();
         if (i + 1 < n_my) {
             make_src(i + 1);
             prologue_t();
