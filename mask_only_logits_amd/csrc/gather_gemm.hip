@@ -1417,6 +1417,31 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
                 prologue_t();
             continue;
         }
+        if constexpr (RED_IN_STAGE && NIMM == NST) {
+            // The per-row consumer with a third stage, in the order of the logits path above:
+            // what touches no LDS before the tile-end barrier, then the partials (which need
+            // the other waves' halves from LDS) and the row ids, then the next tile's first
+            // requests, so that its first wait covers its first K tile and not the second.
+            if constexpr (STORE) {
+                pm0 = cm0;
+                pv0 = cv0;
+                pack();
+#pragma unroll
+                for (int j = 0; j < NST; ++j)
+                    store_one(j);
+            } else {
+                zero_acc();
+            }
+            if (i + 1 < n_my)
+                make_src(i + 1);
+            wait_vmcnt<63>();
+            barrier_no_fence();
+            reduce_part2(cm0, cv0);
+            load_hidx(i + 2);
+            if (i + 1 < n_my)
+                prologue_t();
+            continue;
+        }
         wait_vmcnt<63>();
         barrier_no_fence();
         if (i + 1 < n_my) {
