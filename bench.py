@@ -290,9 +290,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--count-on-host", action="store_true",
-                    help="single-launch logits workloads: read the masked count back to the host before "
-                         "the GEMM (mosaic_masked_logits) instead of letting the kernel read it on the device "
-                         "(mosaic_masked_logits_device_count, the default there)")
+                    help="single-launch logits and argmax_lse workloads: read the masked count back to the "
+                         "host before the GEMM (mosaic_masked_logits, mosaic_masked_logits_argmax_lse) instead "
+                         "of letting the kernel read it on the device (mosaic_masked_logits_device_count, "
+                         "mosaic_masked_logits_argmax_lse_device_count: the default there)")
     ap.add_argument("--profile-copy-mib", type=int, default=0,
                     help="after the timed steps, run a plain elementwise copy of this many MiB three times "
                          "(a kernel of known traffic that calibrates rocprofv3's FETCH_SIZE/WRITE_SIZE)")
@@ -397,12 +398,12 @@ def main():
         variant = mosaic.mosaic_logits_variant(rows_per_launch, V, d, H.dtype, out_dtype)
         log(f"[bench] M={M} chunk_rows={C} launches={launches} variant={variant} "
             f"out={out.numel() * out.element_size() / 1e9:.2f} GB")
-    # One launch on the default persistent kernel: the kernel reads the count the compaction
-    # left in device memory, so the step has no device-to-host read-back (the output buffer
-    # was sized once, from the first count, as a denoising loop whose masked set only
-    # shrinks can do).
-    count_on_device = (args.path == "logits" and launches == 1 and not args.count_on_host and
-                       variant == DEVICE_COUNT_VARIANT)
+    # One launch on the default persistent kernel (logits, or the per-row consumer): the
+    # kernel reads the count the compaction left in device memory, so the step has no
+    # device-to-host read-back (the output buffers were sized once, from the first count, as a
+    # denoising loop whose masked set only shrinks can do).
+    count_on_device = (launches == 1 and not args.count_on_host and
+                       ((args.path == "logits" and variant == DEVICE_COUNT_VARIANT) or consumer))
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -420,7 +421,11 @@ def main():
         m = M if count_on_device else int(cdev.item())     # device -> host: sizes the GEMM
         if i is not None:
             ev[i][1].record(stream)
-        if consumer:
+        if consumer and count_on_device:
+            mosaic.mosaic_masked_logits_argmax_lse_device_count(H, idx, W, cdev, max_rows=M, row_max=rmax,
+                                                                row_argmax=rarg, row_lse=rlse, workspace=ws,
+                                                                stream=stream)
+        elif consumer:
             mosaic.mosaic_masked_logits_argmax_lse(H, idx, W, M=m, chunk_rows=C, row_max=rmax, row_argmax=rarg,
                                                    row_lse=rlse, workspace=ws, stream=stream)
         elif fp8:
