@@ -158,3 +158,52 @@ def test_consumer_count_is_clamped(m):
         torch.cuda.synchronize()
         assert torch.equal(ra[:rows], fa[:rows]), c
         assert bool((ra[rows:] == -7).all()), c
+
+
+def test_compaction_and_consumer_in_one_graph(m):
+    # The per-row consumer with the count read on the device, captured with the compaction in
+    # one graph and replayed as the mask changes (eager work and synchronisation in between);
+    # every replay equals the eager call that takes M from the host, bit for bit, and leaves
+    # the rows at or past the count untouched.
+    L, d, V = 2500, 192, 1700
+    wl = inputs.make_random(93, L=L, d=d, V=V, M=1500, dtype="bf16")
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    tokens = wl.tokens.to(DEV).clone()
+    idx = torch.empty(L, dtype=torch.int32, device=DEV)
+    cnt = torch.empty(1, dtype=torch.int32, device=DEV)
+    rm = torch.empty(L, dtype=torch.float32, device=DEV)
+    ra = torch.empty(L, dtype=torch.int32, device=DEV)
+    rl = torch.empty(L, dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(16, m.mosaic_logits_argmax_lse_workspace_bytes(L, 0, V)), dtype=torch.uint8, device=DEV)
+
+    def run():
+        m.mosaic_mask_compact(tokens, wl.mask_id, idx=idx, count=cnt)
+        m.mosaic_masked_logits_argmax_lse_device_count(H, idx, W, cnt, max_rows=L, row_max=rm, row_argmax=ra,
+                                                       row_lse=rl, workspace=ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                                     # eager run on the capture stream
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    rng = np.random.default_rng(11)
+    for ratio in (0.8, 0.2, 0.0, 0.55):
+        t = rng.integers(0, wl.mask_id, size=L).astype(np.int32)
+        t[rng.random(L) < ratio] = wl.mask_id
+        tokens.copy_(torch.from_numpy(t).to(DEV))
+        for buf, val in ((rm, -3.0), (ra, -7), (rl, -5.0)):
+            buf.fill_(val)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = oracle.mask_compact(torch.from_numpy(t), wl.mask_id)
+        M = int(cnt.item())
+        assert M == want.size
+        if M:
+            hm, ha, hl, _ = m.mosaic_masked_logits_argmax_lse(H, torch.from_numpy(want).to(DEV), W, M=M)
+            torch.cuda.synchronize()
+            assert torch.equal(rm[:M], hm) and torch.equal(ra[:M], ha) and torch.equal(rl[:M], hl), ratio
+        assert bool((rm[M:] == -3.0).all()) and bool((ra[M:] == -7).all()) and bool((rl[M:] == -5.0).all()), ratio
