@@ -170,9 +170,10 @@ def test_headline_shape_sampled_rows(m):
         assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("name", ["ragged", "lowm", "llada_step"])
+@pytest.mark.parametrize("name", ["ragged", "lowm", "llada_step", "long_ffn"])
 def test_other_workloads_sampled_rows(m, name):
-    # Dream-shaped (d = 3584, V = 152064) ragged batch and low-M case, and the LLaDA step
+    # Dream-shaped (d = 3584, V = 152064) ragged batch and low-M case, the LLaDA step, and
+    # the FFN-dominant workload in its 8192-row chunks
     wl = inputs.make_workload(name)
     if wl.seq_offsets is not None:
         idx = oracle.mask_compact_batched(wl.tokens, wl.seq_offsets, wl.mask_id)[0]

@@ -115,6 +115,27 @@ def test_headline_shape_sampled_rows(m):
     assert_close(out[torch.from_numpy(rows).to(DEV)], ref, "fp8 long_logits sampled rows")
 
 
+@pytest.mark.parametrize("name", ["llada_step", "ragged"])
+def test_other_workloads_sampled_rows(m, name):
+    # the LLaDA step (one 1229-row chunk) and the Dream-shaped ragged batch (d = 3584,
+    # V = 152064, one 21399-row launch in CSR order) through the FP8 LM head
+    wl = inputs.make_workload(name)
+    if wl.seq_offsets is not None:
+        idx = oracle.mask_compact_batched(wl.tokens, wl.seq_offsets, wl.mask_id)[0]
+    else:
+        idx = oracle.mask_compact(wl.tokens, wl.mask_id)
+    Wq, ws = m.mosaic_quantize_rows_fp8(wl.W.to(DEV))
+    out = m.mosaic_masked_logits_fp8(wl.H.to(DEV), torch.from_numpy(idx).to(DEV), Wq, ws,
+                                     chunk_rows=wl.chunk_rows)
+    torch.cuda.synchronize()
+    rows = sample_rows(idx.size, wl.chunk_rows, 4, seed=13)
+    rows = rows[np.linspace(0, rows.size - 1, min(rows.size, 10)).astype(int)]
+    qh, sh = oracle.quantize_rows_e4m3(wl.H, idx)
+    qw, sw = oracle.quantize_rows_e4m3(wl.W)
+    ref = oracle.logits_fp8(qh, sh, qw, sw, rows=rows)
+    assert_close(out[torch.from_numpy(rows).to(DEV)], ref, f"fp8 {name} sampled rows")
+
+
 def test_dream_shape_low_m_all_rows(m):
     # the low-M workload (Dream-shaped LM head: d = 3584, V = 152064; M = 20), every row
     wl = inputs.make_workload("lowm")
