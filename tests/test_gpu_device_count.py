@@ -207,3 +207,27 @@ def test_compaction_and_consumer_in_one_graph(m):
             torch.cuda.synchronize()
             assert torch.equal(rm[:M], hm) and torch.equal(ra[:M], ha) and torch.equal(rl[:M], hl), ratio
         assert bool((rm[M:] == -3.0).all()) and bool((ra[M:] == -7).all()) and bool((rl[M:] == -5.0).all()), ratio
+
+
+def test_ragged_batch_count_from_csr(m):
+    # A ragged batch, as the bench's ragged step runs it: the CSR compaction's last offset
+    # (the batch's masked total) is the count the logits kernel and the consumer read.
+    L, d, V = 6000, 256, 3000
+    wl = inputs.make_random(97, L=L, d=d, V=V, M=3900, dtype="bf16", nseq=7)
+    tokens, offs = wl.tokens.to(DEV), wl.seq_offsets.to(DEV)
+    H, W = wl.H.to(DEV), wl.W.to(DEV)
+    idx, idx_offsets = m.mosaic_mask_compact_batched(tokens, offs, wl.mask_id)
+    cnt = idx_offsets[-1:]
+    out = _poisoned(L, V)
+    m.mosaic_masked_logits_device_count(H, idx, W, cnt, max_rows=L, out=out)
+    rm, ra, rl, _ = m.mosaic_masked_logits_argmax_lse_device_count(H, idx, W, cnt, max_rows=L)
+    M = int(cnt.item())
+    want_idx, want_offs = oracle.mask_compact_batched(wl.tokens, wl.seq_offsets, wl.mask_id)
+    assert M == want_idx.size and np.array_equal(idx_offsets.cpu().numpy(), want_offs)
+    ref = m.mosaic_masked_logits(H, idx, W, M=M)
+    hm, ha, hl, _ = m.mosaic_masked_logits_argmax_lse(H, idx, W, M=M)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:M], ref) and bool((out[M:].float() == POISON).all())
+    assert torch.equal(rm[:M], hm) and torch.equal(ra[:M], ha) and torch.equal(rl[:M], hl)
+    rows = sample_rows(M, 0, 12)
+    assert_close(out[torch.as_tensor(rows, device=DEV)], oracle.masked_logits(wl.H, want_idx[rows], wl.W), "ragged devcount")
