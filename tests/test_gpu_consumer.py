@@ -187,6 +187,34 @@ def test_other_workloads_sampled_rows(m, name):
     _check(got, wl.H, idx, wl.W, rows=rows, what=name)
 
 
+@pytest.mark.parametrize("name", ["long_logits", "ragged"])
+def test_one_hot_w_full_shape(m, name):
+    # W[v] = e_(v mod d) at full size, logits not stored: row i's logits are the gathered
+    # H[idx[i], v mod d], exact in fp32, so its max is the gathered row's largest element
+    # and its argmax the first column k attaining it (column k first appears at v = k), both
+    # bit for bit on every row; its lse is log(sum_k c_k exp(H[idx[i], k])) with c_k the
+    # number of v < V with v mod d == k, held to the bound above
+    wl = inputs.make_workload(name)
+    d, V = wl.d, wl.V
+    if wl.seq_offsets is not None:
+        idx = oracle.mask_compact_batched(wl.tokens, wl.seq_offsets, wl.mask_id)[0]
+    else:
+        idx = oracle.mask_compact(wl.tokens, wl.mask_id)
+    W1 = inputs.one_hot_rows(V, d).to(DEV)
+    mx, am, lse, _ = m.mosaic_masked_logits_argmax_lse(wl.H.to(DEV), torch.from_numpy(idx).to(DEV), W1,
+                                                        chunk_rows=wl.chunk_rows)
+    torch.cuda.synchronize()
+    h = wl.H[torch.from_numpy(idx).long()].float().numpy()             # [M, d], exact
+    assert np.array_equal(mx.cpu().numpy(), h.max(axis=1))
+    assert np.array_equal(am.cpu().numpy(), h.argmax(axis=1))         # first occurrence
+    c = np.full(d, V // d, dtype=np.float64) + (np.arange(d) < V % d)
+    hd = h.astype(np.float64)
+    top = hd.max(axis=1)
+    want = top + np.log((np.exp(hd - top[:, None]) * c).sum(axis=1))
+    got = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - want) <= TOL * np.maximum(1.0, np.abs(want))), np.abs(got - want).max()
+
+
 @pytest.mark.parametrize("L,d,V,M,C", [CASES[0], CASES[2], CASES[4], CASES[6]])
 def test_mfma_forms_match(m, lib_env, L, d, V, M, C):
     # the 32 x 32 x 16 MFMA form of the fused kernel (variant=16) against the default

@@ -136,6 +136,38 @@ def test_other_workloads_sampled_rows(m, name):
     assert_close(out[torch.from_numpy(rows).to(DEV)], ref, f"fp8 {name} sampled rows")
 
 
+@pytest.mark.parametrize("name", ["long_logits", "ragged", "llada_step"])
+def test_one_hot_w_full_shape_bit_exact(m, name):
+    # W[v] = 448 e_(v mod d): each W row quantizes to the single code of 448 with row scale
+    # exactly 1, so each logit is one exact product, value(Hq[i, v mod d]) * 448, times the
+    # H row's scale in fp32 and rounded to bf16.  Every element of the full-size output is
+    # then fixed by the oracle's quantization of the gathered H rows.
+    wl = inputs.make_workload(name)
+    d, V = wl.d, wl.V
+    if wl.seq_offsets is not None:
+        idx = oracle.mask_compact_batched(wl.tokens, wl.seq_offsets, wl.mask_id)[0]
+    else:
+        idx = oracle.mask_compact(wl.tokens, wl.mask_id)
+    M = idx.size
+    W1 = (inputs.one_hot_rows(V, d, dtype="f32") * 448.0).to(torch.bfloat16)
+    Wq, ws = m.mosaic_quantize_rows_fp8(W1.to(DEV))
+    code448 = oracle.e4m3_encode(448.0)
+    cols = torch.arange(V, device=DEV) % d
+    want_q = torch.zeros((V, d), dtype=torch.uint8, device=DEV)
+    want_q[torch.arange(V, device=DEV), cols] = code448
+    assert torch.equal(Wq, want_q) and torch.all(ws == 1.0)
+    del want_q, W1
+    out = m.mosaic_masked_logits_fp8(wl.H.to(DEV), torch.from_numpy(idx).to(DEV), Wq, ws,
+                                     chunk_rows=wl.chunk_rows)
+    torch.cuda.synchronize()
+    qh, sh = oracle.quantize_rows_e4m3(wl.H, idx)
+    lut = torch.tensor([oracle.e4m3_value(c) for c in range(256)], dtype=torch.float32)
+    T = ((lut[torch.from_numpy(qh).long()] * 448.0) * torch.from_numpy(sh)[:, None]).to(torch.bfloat16).to(DEV)
+    for r0 in range(0, M, 2048):
+        r1 = min(M, r0 + 2048)
+        assert torch.equal(out[r0:r1], T[r0:r1][:, cols]), (name, r0)
+
+
 def test_dream_shape_low_m_all_rows(m):
     # the low-M workload (Dream-shaped LM head: d = 3584, V = 152064; M = 20), every row
     wl = inputs.make_workload("lowm")
