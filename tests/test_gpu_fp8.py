@@ -168,6 +168,41 @@ def test_one_hot_w_full_shape_bit_exact(m, name):
         assert torch.equal(out[r0:r1], T[r0:r1][:, cols]), (name, r0)
 
 
+@pytest.mark.parametrize("name", ["long_logits", "ragged"])
+def test_one_hot_h_full_shape_bit_exact(m, name):
+    # H[p] = e_(p mod d): each gathered H row quantizes to the code of 448 at column
+    # idx[i] mod d with the oracle's row scale s_h, so logit (i, v) is one exact product,
+    # value(Wq[v, idx[i] mod d]) * 448, times (s_h * s_w[v]) in fp32 (the kernel's order),
+    # rounded to bf16.  Every element of the full-size output is then fixed by the oracle's
+    # quantization of W.
+    wl = inputs.make_workload(name)
+    d, V = wl.d, wl.V
+    if wl.seq_offsets is not None:
+        idx = oracle.mask_compact_batched(wl.tokens, wl.seq_offsets, wl.mask_id)[0]
+    else:
+        idx = oracle.mask_compact(wl.tokens, wl.mask_id)
+    M = idx.size
+    H1 = inputs.one_hot_rows(wl.L, d)
+    qh, sh = oracle.quantize_rows_e4m3(H1, idx)
+    code448 = oracle.e4m3_encode(448.0)
+    assert np.all(qh[np.arange(M), idx % d] == code448) and np.count_nonzero(qh) == M
+    assert np.all(sh == sh[0])
+    Wq, ws = m.mosaic_quantize_rows_fp8(wl.W.to(DEV))
+    qw, sw = oracle.quantize_rows_e4m3(wl.W)
+    assert np.array_equal(Wq.cpu().numpy(), qw) and np.array_equal(ws.cpu().numpy(), sw)
+    out = m.mosaic_masked_logits_fp8(H1.to(DEV), torch.from_numpy(idx).to(DEV), Wq, ws,
+                                     chunk_rows=wl.chunk_rows)
+    torch.cuda.synchronize()
+    lut = torch.tensor([oracle.e4m3_value(c) for c in range(256)], dtype=torch.float32, device=DEV)
+    Wt = (lut[Wq.long()] * 448.0).T.contiguous()                      # [d, V], exact
+    hw = (torch.from_numpy(sh[:1]) * torch.from_numpy(sw)).to(DEV)    # s_h * s_w[v] in fp32
+    kcol = torch.from_numpy(idx % d).to(DEV).long()
+    for r0 in range(0, M, 2048):
+        r1 = min(M, r0 + 2048)
+        want = (Wt[kcol[r0:r1]] * hw[None, :]).to(torch.bfloat16)
+        assert torch.equal(out[r0:r1], want), (name, r0)
+
+
 def test_dream_shape_low_m_all_rows(m):
     # the low-M workload (Dream-shaped LM head: d = 3584, V = 152064; M = 20), every row
     wl = inputs.make_workload("lowm")
