@@ -136,9 +136,9 @@ __global__ __launch_bounds__(kThreads) void mask_compact_kernel(const T *__restr
         uint32_t before = 0, tile_total = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const uint32_t c = wave_count[w];
-            before += (w < wave) ? c : 0u;
-            tile_total += c;
+            const uint32_t cw = wave_count[w];
+            before += (w < wave) ? cw : 0u;
+            tile_total += cw;
         }
         __syncthreads();   // wave_count is rewritten by the next tile
 
