@@ -784,7 +784,7 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
     constexpr int H_TILE = BM * ROW_BYTES;
     // LDS: the two W stages (32 KiB each), then the two H stages; a refill requests H's
     // rows before W's.  Against alternating W and H stages with W first, measured on one
-    // box: +0.5-1% for the 16 x 16 x 32 form, -2% for the 32 x 32 x 16 form.
+    // MI355X: +0.5-1% for the 16 x 16 x 32 form, -2% for the 32 x 32 x 16 form.
     constexpr int H_BASE = WST * W_TILE;
     constexpr int WV = BV / 2, WM = BM / (NW / 2);
     constexpr int MB = M16 ? 16 : 32;         // MFMA block edge
@@ -1558,7 +1558,7 @@ __global__ __launch_bounds__(1024) void logits_reduce_finish_kernel(const float 
 // Cache-policy operand of global_load_lds for data read exactly once: the NT (streaming)
 // bit of gfx950's cache policy.  The low-M kernels read W once per launch; with this bit
 // on W's requests the 20-row workload's launch went from 195-196 us to 177-179 us
-// (rocprofv3, one box), while H, which every step re-reads, keeps the default policy.
+// (rocprofv3, one MI355X), while H, which every step re-reads, keeps the default policy.
 constexpr int kLoadStreaming = 2;
 
 
