@@ -1010,9 +1010,16 @@ gather_gemm_bf16_defer_kernel(const __bf16 *__restrict__ H, const int32_t *__res
                 bf16x8_t nxt;
                 if (early)
                     nxt = *(const bf16x8_t *)(smem + ab + a * MB * ROW_BYTES);
+                // odd rows take the B blocks in reverse, so consecutive MFMAs always share
+                // one operand (a row's last B block is the next row's first): fewer operand
+                // bits change, which lowers the power per MFMA and lets the clock rise
+                // (+0.4-0.9% on 1229 to 21399 rows, two MI355Xs; each block's k order, and so
+                // every result bit, is unchanged)
 #pragma unroll
-                for (int bm = 0; bm < AM; ++bm)
+                for (int c = 0; c < AM; ++c) {
+                    const int bm = (a & 1) ? AM - 1 - c : c;
                     acc[a][bm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][a], bf[cur][bm], acc[a][bm], 0, 0, 0);
+                }
                 af[0][a] = early ? nxt : *(const bf16x8_t *)(smem + ab + a * MB * ROW_BYTES);
             }
         } else {
